@@ -1,0 +1,75 @@
+"""Pure-Python brute-force references used to pin the oracle on tiny inputs.
+
+These are independent of ``oracle/``: element-by-element loops over Python
+ints and floats, no numpy vectorisation, no matmul. They exist only to check
+the oracle, and are far too slow for anything but tiny shapes.
+"""
+import math
+import struct
+
+
+def brute_align(topk_ids, E, b, capacity):
+    """Sort-based alignment: valid routes sorted by (expert ID, route ID)."""
+    flat = [int(e) for row in topk_ids for e in row]
+    mk = len(flat)
+    valid = [r for r in range(mk) if 0 <= flat[r] < E]
+    order = sorted(valid, key=lambda r: (flat[r], r))
+    rows, blocks = [], []
+    i = 0
+    while i < len(order):
+        e = flat[order[i]]
+        j = i
+        while j < len(order) and flat[order[j]] == e:
+            j += 1
+        seg = order[i:j]
+        while len(seg) % b:
+            seg = seg + [mk]
+        rows.extend(seg)
+        blocks.extend([e] * (len(seg) // b))
+        i = j
+    n = len(rows)
+    rows += [mk] * (capacity - n)
+    blocks += [-1] * (capacity // b - len(blocks))
+    return rows, blocks, n
+
+
+def bf16_bits_to_float(bits):
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def deq_elem(q, s, z, g, e, n, kk):
+    word = int(q[e][n][kk // 8])
+    nib = (word >> (4 * (kk % 8))) & 0xF
+    return (nib - int(z[e][n][kk // g])) * float(s[e][n][kk // g])
+
+
+def brute_ffn(x_bits, topk_ids, topk_w, w13, w2, E):
+    """y[t][h] by explicit loops over tokens, routes, neurons and elements."""
+    M = len(topk_ids)
+    k = len(topk_ids[0])
+    H = len(x_bits[0])
+    I = w13.N // 2
+    q13, s13, z13, g13 = w13.q.tolist(), w13.s.astype(float).tolist(), w13.z.tolist(), w13.g
+    q2, s2, z2, g2 = w2.q.tolist(), w2.s.astype(float).tolist(), w2.z.tolist(), w2.g
+    y = [[0.0] * H for _ in range(M)]
+    for t in range(M):
+        x = [bf16_bits_to_float(v) for v in x_bits[t]]
+        for j in range(k):
+            e = int(topk_ids[t][j])
+            if not (0 <= e < E):
+                continue
+            wt = float(topk_w[t][j])
+            a = []
+            for i in range(I):
+                gate = 0.0
+                up = 0.0
+                for h in range(H):
+                    gate += x[h] * deq_elem(q13, s13, z13, g13, e, i, h)
+                    up += x[h] * deq_elem(q13, s13, z13, g13, e, I + i, h)
+                a.append(gate / (1.0 + math.exp(-gate)) * up)
+            for h in range(H):
+                acc = 0.0
+                for i in range(I):
+                    acc += a[i] * deq_elem(q2, s2, z2, g2, e, h, i)
+                y[t][h] += wt * acc
+    return y
