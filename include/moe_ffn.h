@@ -1,0 +1,175 @@
+/*
+ * moe_ffn.h — C ABI of the MI355X (gfx950) routed MoE expert-FFN layer.
+ *
+ * The layer computes, for M tokens each routed to k of E experts,
+ *   (1) route alignment: group the M*k flattened routes by expert in route-ID
+ *       order, pad each expert's count to a multiple of b, and emit the
+ *       expert-block vector;
+ *   (2) gate/up projection over packed 4-bit AWQ-style group-quantised expert
+ *       weights with the SwiGLU activation silu(gate) * up;
+ *   (3) the down projection;
+ *   (4) the router-weighted top-k combine.
+ * Steps (1) and the packed-weight format follow "Route-Block Membership Selects
+ * Packed-AWQ Arithmetic" (arXiv 2607.26316: first paragraph, the A_e / B(e,j)
+ * paragraph, the stable-construction paragraph, and the fixture paragraph for
+ * 4-bit AWQ with group 128). Steps (2)-(4) follow "Hardware-Native Joint
+ * Sparse-Quantization for Trillion-Scale MoE" (arXiv 2610.02241, Sections 2,
+ * 3.3 with Eq. 4, 3.4) and the warp-decode write-up (cursor.com blog, "Cómo
+ * funcionan los dos kernels").
+ *
+ * Conventions for every entry point:
+ *   - Every array pointer is DEVICE memory owned by the caller. The library
+ *     allocates nothing, keeps no pointer after returning, and never
+ *     synchronises the host: work is enqueued on `stream` and the buffers must
+ *     stay valid until it completes.
+ *   - Host-checkable errors return a status synchronously and enqueue nothing.
+ *     Launch failures return MOE_ERR_HIP. M == 0 is a no-op returning MOE_OK.
+ *   - Data-dependent conditions are defined behaviour, not errors: an expert
+ *     ID outside [0, E) marks an invalid route, which alignment skips and
+ *     which contributes nothing to the output.
+ *   - Results are deterministic: the same inputs, shapes and path give the
+ *     same output bytes on every run and for every workgroup cap (no
+ *     floating-point atomics; every reduction has a fixed order).
+ *   - Route IDs are the row-major flattening r = t*k + j of the [M][k]
+ *     top-k arrays; token(r) = r / k.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent sizes */
+  MOE_ERR_UNSUPPORTED = 2,  /* shape/format/path combination not implemented */
+  MOE_ERR_CAPACITY = 3,     /* alignment buffers smaller than moe_align_capacity */
+  MOE_ERR_WORKSPACE = 4,    /* workspace smaller than moe_ffn_workspace_size */
+  MOE_ERR_HIP = 5           /* a HIP launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_W_INT4_AWQ = 0,  /* q: uint32 [E][N][K/8], element kk in bits 4*(kk%8)..+3;
+                          scale: fp16 [E][N][K/group]; zero: uint8 [E][N][K/group] in 0..15;
+                          w = (q - zero) * scale */
+  MOE_W_MXFP8 = 1      /* q: uint8 OCP E4M3FN [E][N][K]; scale: uint8 E8M0 [E][N][K/32];
+                          zero: NULL; w = e4m3(q) * 2^(scale - 127); group must be 32 */
+} moe_wfmt;
+
+typedef enum {
+  MOE_PATH_AUTO = 0,     /* decode for M <= moe_ffn_auto_decode_max_m(), else grouped */
+  MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
+  MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised bf16 MFMA grouped GEMMs + combine */
+} moe_path;
+
+/* One projection's resident packed weights for all E experts. */
+typedef struct {
+  int32_t fmt;          /* moe_wfmt */
+  int32_t group;        /* elements per scale group along K (int4: multiple of 32; mxfp8: 32) */
+  const void* q;        /* packed values, layout per moe_wfmt */
+  const void* scale;    /* per-group scales, layout per moe_wfmt */
+  const uint8_t* zero;  /* int4 zero points, NULL for MXFP8 */
+} moe_weights;
+
+/* Layer description. W13 has N = 2*I rows (rows 0..I-1 gate, I..2I-1 up) and
+ * K = H; W2 has N = H rows and K = I. Both projections must use the same fmt. */
+typedef struct {
+  int32_t M;               /* tokens (>= 0) */
+  int32_t H;               /* hidden size, multiple of 32 and of w13.group */
+  int32_t I;               /* per-expert intermediate size, multiple of 32 and of w2.group */
+  int32_t E;               /* experts (1..2048) */
+  int32_t k;               /* experts per token (1..E) */
+  int32_t b;               /* alignment block size used by the grouped path (>= 1) */
+  moe_weights w13;
+  moe_weights w2;
+  int32_t path;            /* moe_path */
+  int32_t max_workgroups;  /* 0: library default grid. > 0: cap on workgroups per launch.
+                              Output bytes do not depend on it. */
+} moe_ffn_desc;
+
+/* Number of int32 entries sorted_route_ids needs: roundup(M*k + min(E, M*k)*(b-1), b).
+ * expert_block_ids needs capacity / b entries. Host-only and pure; returns 0 when
+ * M < 0, k < 1, E < 1 or b < 1. */
+size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
+
+/* Step (1), route alignment ("Route-Block Membership Selects Packed-AWQ
+ * Arithmetic": first paragraph; A_e / B(e,j) paragraph; stable-construction
+ * paragraph).
+ *   topk_ids          [M*k] int32, row-major [M][k]
+ *   sorted_route_ids  [capacity] out: for each expert e ascending, its valid route
+ *                     IDs in ascending order, then the sentinel M*k up to a multiple
+ *                     of b; positions num_padded..capacity-1 hold the sentinel.
+ *   expert_block_ids  [capacity/b] out: expert of each b-row block; -1 past the end.
+ *   num_padded        [1] out: total aligned rows, sum_e ceil(c_e/b)*b.
+ * Runs as one workgroup (M*k up to 2^24 routes, E <= 2048).
+ * Errors: MOE_ERR_INVALID_ARG (null pointers, M < 0, k < 1, E < 1, b < 1),
+ * MOE_ERR_UNSUPPORTED (E > 2048 or M*k > 2^24), MOE_ERR_CAPACITY (capacity too small). */
+moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
+                     int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
+                     size_t capacity, hipStream_t stream);
+
+/* Bytes of device workspace moe_ffn_forward needs for this description (path
+ * resolved as moe_ffn_forward resolves it). Errors as moe_ffn_forward's
+ * validation. */
+moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes);
+
+/* Steps (1)-(4): y = sum_j w[t,j] * W2[e] (silu(W13g[e] x_t) * W13u[e] x_t).
+ *   x         [M][H] bf16 bit patterns
+ *   topk_ids  [M][k] int32 expert IDs (out-of-range IDs are skipped)
+ *   topk_w    [M][k] fp32 combine weights, used as given
+ *   y         [M][H] fp32, overwritten
+ *   ws        workspace of at least moe_ffn_workspace_size bytes, 256-byte aligned
+ * The decode path needs no alignment (the output-stationary design of the
+ * warp-decode write-up, "Eliminación del relleno"); the grouped path runs
+ * moe_align into the workspace first. The fp32 route-indexed intermediate
+ * silu(gate)*up [M*k][I] is left in the workspace at moe_ffn_intermediate_offset.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                           const float* topk_w, float* y, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Grouped path on a caller-supplied alignment (same layout and meaning as
+ * moe_align's outputs, with the given capacity). Lets a caller reorder routes
+ * within an expert's rows: the output bytes must not change. Route entries
+ * outside [0, M*k) are padding; blocks whose expert is outside [0, E) are skipped.
+ * Each valid route must appear at most once. Errors as moe_ffn_forward. */
+moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
+                                   const int32_t* topk_ids, const float* topk_w,
+                                   const int32_t* sorted_route_ids,
+                                   const int32_t* expert_block_ids,
+                                   const int32_t* num_padded, size_t capacity, float* y,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Same as moe_ffn_forward, and records events[0] before the first kernel and
+ * events[i+1] after kernel i (n_events must be moe_ffn_kernel_count + 1) so a
+ * caller can time each kernel on the stream. Events are caller-created. */
+moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
+                                    const int32_t* topk_ids, const float* topk_w, float* y,
+                                    void* ws, size_t ws_bytes, hipStream_t stream,
+                                    hipEvent_t* events, int32_t n_events);
+
+/* Number of kernels moe_ffn_forward launches for this description (0 on error). */
+int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
+
+/* Name of kernel i of moe_ffn_forward for this description, or NULL. */
+const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
+
+/* Byte offset inside the workspace of the fp32 [M*k][I] intermediate. */
+moe_status moe_ffn_intermediate_offset(const moe_ffn_desc* d, size_t* offset);
+
+/* Largest M for which MOE_PATH_AUTO picks the decode path. */
+int32_t moe_ffn_auto_decode_max_m(void);
+
+/* Static string for a status code. */
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -89,15 +89,22 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+# AWQ's interleaved packing: nibble slot i (bits 4i..4i+3) of a word holds
+# element AWQ_ORDER[i] of that word's eight elements.
+AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
 def unpack_int4(qwords: np.ndarray) -> np.ndarray:
     """uint32 words [..., K/8] -> unsigned 4-bit values [..., K].
 
-    Element kk is bits [4*(kk % 8), 4*(kk % 8) + 4) of word kk // 8.
+    Word kk // 8 holds elements 8*(kk // 8) .. +7; element AWQ_ORDER[i] sits in
+    nibble slot i (bits 4i..4i+3).
     """
     w = np.asarray(qwords, dtype=np.uint32)
-    shifts = (4 * np.arange(8, dtype=np.uint32))
-    nib = (w[..., None] >> shifts) & np.uint32(15)
-    return nib.reshape(*w.shape[:-1], w.shape[-1] * 8).astype(np.int64)
+    slots = (w[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & np.uint32(15)
+    out = np.empty_like(slots)
+    out[..., list(AWQ_ORDER)] = slots
+    return out.reshape(*w.shape[:-1], w.shape[-1] * 8).astype(np.int64)
 
 
 def dequant_int4(qwords: np.ndarray, scales: np.ndarray, zeros: np.ndarray,

@@ -39,7 +39,9 @@ def bf16_bits_to_float(bits):
 
 def deq_elem(q, s, z, g, e, n, kk):
     word = int(q[e][n][kk // 8])
-    nib = (word >> (4 * (kk % 8))) & 0xF
+    j = kk % 8
+    # even element 2m in nibble slot m, odd element 2m+1 in slot m+4
+    nib = (word >> (4 * (j >> 1) + 16 * (j & 1))) & 0xF
     return (nib - int(z[e][n][kk // g])) * float(s[e][n][kk // g])
 
 

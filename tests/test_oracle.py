@@ -155,7 +155,7 @@ def test_dequant_hand_worked(case):
 
 
 def test_dequant_all_q_z_pairs():
-    # Every (q, z) pair: 16 words, word q repeats nibble q eight times.
+    # Every (q, z) pair: 16 words, word q repeats nibble q in all eight slots.
     words = np.array([[int(f"{q:x}" * 8, 16)] for q in range(16)], dtype=np.uint32)
     for zv in range(16):
         for sv in (0.5, 0.0029296875, 0.01):

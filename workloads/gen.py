@@ -11,9 +11,10 @@ the warp-decode blog ("La ruta convencional de MoE"). No trained weights are
 used: every array is drawn from a seeded numpy PCG64 generator.
 
 Conventions shared by both consumers (they define the input bytes only):
-  * int4 weights: uint32 words ``q[e, n, kk // 8]``; element ``kk`` sits in
-    bits ``[4*(kk % 8), 4*(kk % 8) + 4)`` of its word. Drawing every word
-    uniformly from [0, 2^32) draws each nibble independently from U{0..15}.
+  * int4 weights: uint32 words ``q[e, n, kk // 8]`` in AWQ's interleaved
+    nibble order (nibble slot i holds element [0, 2, 4, 6, 1, 3, 5, 7][i] of
+    the word's eight). Drawing every word uniformly from [0, 2^32) draws each
+    nibble independently from U{0..15}, whatever the order.
   * scales: fp16 ``s[e, n, kk // g]``; zero points: uint8 ``z[e, n, kk // g]``
     holding 0..15.
   * W13 has ``2I`` rows: rows ``0..I-1`` are the gate projection, rows
