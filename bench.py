@@ -1,0 +1,286 @@
+"""Benchmark of the routed MoE expert-FFN layer on one MI355X.
+
+Workload (the headline one): single-token decode, M=1, hidden 2048,
+per-expert intermediate 768, 128 experts, top-8, AWQ-style int4 weights with
+group 128 (fp16 scales, uint8 zeros), bf16 activations. A step is one call of
+the whole layer (moe_ffn_forward; at M=1 the automatic path is the
+output-stationary decode path, which has no alignment step by design). Every
+step uses the next of 16 device copies of the packed layer (16 x 316 MB, more
+than the 256 MB Infinity Cache) and the next of 64 seeded routings, so each
+call streams cold weights from HBM. The timed region replays a HIP graph of K
+steps between two synchronised events.
+
+Printed: one JSON line with tokens/s, the per-kernel roofline of the dominant
+kernel (decode gate/up, timed with events around each kernel in a separate
+pass), the oracle's CPU throughput on a bounded sample, and the M=21 / M=256
+layer numbers as extra context.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+N_LAYER_COPIES = 16
+N_ROUTINGS = 64
+FLOPS_PER_ROUTE = None  # set from the shapes: 2 * (2I*H + H*I)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--workload", default="decode_m1")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the M=21 / M=256 context numbers")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+class Rotation:
+    """Device inputs for one workload: layer copies and routings."""
+
+    def __init__(self, name, n_layers, n_routings, seed=0):
+        import torch
+        import mixture_experts_ffn_align_amd as moe
+        from workloads import CONFIGS, make_weights
+        from workloads.gen import make_routing, make_x
+        self.cfg = cfg = CONFIGS[name]
+        w13, w2 = make_weights(cfg, seed, 0)
+        self.w13_host, self.w2_host = w13, w2
+        base13 = moe.DeviceProjection.from_host(w13, "cuda")
+        base2 = moe.DeviceProjection.from_host(w2, "cuda")
+        self.layers = []
+        for i in range(n_layers):
+            p13 = base13 if i == 0 else moe.DeviceProjection(
+                base13.fmt, base13.group, base13.q.clone(), base13.scale.clone(), base13.zero.clone())
+            p2 = base2 if i == 0 else moe.DeviceProjection(
+                base2.fmt, base2.group, base2.q.clone(), base2.scale.clone(), base2.zero.clone())
+            self.layers.append(moe.MoeLayer(p13, p2, cfg.E, cfg.H, cfg.I, cfg.k, cfg.b))
+        self.inputs = []
+        self.host_inputs = []
+        for r in range(n_routings):
+            ids, w = make_routing(cfg, seed, r)
+            x = make_x(cfg, seed, r)
+            self.host_inputs.append((x, ids, w))
+            self.inputs.append((torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16),
+                                torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()))
+        self.y = torch.empty((cfg.M, cfg.H), dtype=torch.float32, device="cuda")
+        d = self.layers[0].desc(cfg.M)
+        self.ws = torch.empty(moe.moe_ffn_workspace_size(d), dtype=torch.uint8, device="cuda")
+        self.touched = [len(np.unique(h[1])) for h in self.host_inputs]
+
+    def step(self, i, profiled_events=None):
+        import mixture_experts_ffn_align_amd as moe
+        layer = self.layers[i % len(self.layers)]
+        x, ids, w = self.inputs[i % len(self.inputs)]
+        d = layer.desc(self.cfg.M)
+        if profiled_events is None:
+            moe.moe_ffn_forward(d, x, ids, w, self.y, self.ws)
+        else:
+            moe.moe_ffn_forward_profiled(d, x, ids, w, self.y, self.ws, profiled_events)
+
+    def expert_bytes(self):
+        return self.w13_host.expert_bytes() + self.w2_host.expert_bytes(), \
+            self.w13_host.expert_bytes(), self.w2_host.expert_bytes()
+
+
+def time_graph(rot, steps, warmup):
+    """Milliseconds for `steps` layer calls replayed from HIP graphs."""
+    import torch
+    stream = torch.cuda.Stream()
+    chunk = min(steps, 1024)
+    graphs = []
+    with torch.cuda.stream(stream):
+        for i in range(3):            # eager warm-up of the code objects
+            rot.step(i)
+    torch.cuda.synchronize()
+
+    def capture(n, start):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                rot.step(start + i)
+        return g
+
+    full, rem = divmod(steps, chunk)
+    g_main = capture(chunk, 0)
+    g_rem = capture(rem, chunk) if rem else None
+    wg = capture(max(1, min(warmup, 1024)), 7) if warmup > 0 else None
+    torch.cuda.synchronize()
+    if wg is not None:
+        for _ in range(max(1, warmup // 1024)):
+            wg.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    t0.record(cur)
+    for _ in range(full):
+        g_main.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    t1.record(cur)
+    torch.cuda.synchronize()
+    del graphs
+    return t0.elapsed_time(t1)
+
+
+def kernel_times(rot, steps):
+    """Average duration (ms) of each kernel of the layer, from events recorded
+    around every kernel on the launch stream, over `steps` eager calls."""
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    d = rot.layers[0].desc(rot.cfg.M)
+    nk = moe.moe_ffn_kernel_count(d)
+    names = [moe.moe_ffn_kernel_name(d, i) for i in range(nk)]
+    sums = np.zeros(nk)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    for i in range(steps):
+        rot.step(i, profiled_events=evs[i])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for j in range(nk):
+            sums[j] += evs[i][j].elapsed_time(evs[i][j + 1])
+    return dict(zip(names, (sums / steps).tolist()))
+
+
+def cpu_baseline(rot, seconds):
+    """The fp64 oracle on the host: tokens/s over a bounded sample of the same
+    workload (rotating routings; one layer)."""
+    import psutil
+    import oracle
+    cfg = rot.cfg
+    proc = psutil.Process()
+    n = 0
+    c0 = proc.cpu_times()
+    t0 = time.perf_counter()
+    while True:
+        x, ids, w = rot.host_inputs[n % len(rot.host_inputs)]
+        oracle.ffn(x, ids, w, rot.w13_host, rot.w2_host, cfg.E)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    wall = time.perf_counter() - t0
+    c1 = proc.cpu_times()
+    busy = (c1.user - c0.user) + (c1.system - c0.system)
+    return {
+        "value": n * cfg.M / wall, "unit": "tokens/s",
+        "cores": max(1, int(math.ceil(busy / wall - 0.05))),
+        "kind": "oracle",
+        "sample": f"{n} layer calls of the {cfg.name} workload (M={cfg.M}) on one layer, "
+                  f"{wall:.1f} s wall, {busy / wall:.2f} average busy threads "
+                  f"of {len(os.sched_getaffinity(0))} available",
+    }
+
+
+def layer_numbers(rot, steps):
+    ms = time_graph(rot, steps, warmup=min(steps, 64))
+    t = ms / steps * 1e-3
+    cfg = rot.cfg
+    per_expert, _, _ = rot.expert_bytes()
+    touched = float(np.mean([rot.touched[i % len(rot.touched)] for i in range(steps)]))
+    bytes_per_call = touched * per_expert
+    flops = cfg.M * cfg.k * 2 * (2 * cfg.I * cfg.H + cfg.H * cfg.I)
+    return {
+        "tokens_per_s": cfg.M / t, "us_per_layer": t * 1e6,
+        "effective_weight_GBps": bytes_per_call / t / 1e9,
+        "hbm_frac": bytes_per_call / t / 1e9 / HBM_PEAK_GBPS,
+        "mfma_frac_bf16": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+        "touched_experts_mean": touched,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import mixture_experts_ffn_align_amd as moe
+    moe.lib()  # fail loudly if the HIP library is missing
+
+    log("preparing", args.workload)
+    rot = Rotation(args.workload, N_LAYER_COPIES, N_ROUTINGS)
+    cfg = rot.cfg
+    log("timing", args.steps, "steps")
+    ms = time_graph(rot, args.steps, args.warmup)
+    t_step = ms / args.steps
+    tokens_s = cfg.M * args.steps / (ms * 1e-3)
+    per_expert, b13, b2 = rot.expert_bytes()
+    touched = float(np.mean([rot.touched[i % N_ROUTINGS] for i in range(args.steps)]))
+    layer_gbps = touched * per_expert / (t_step * 1e-3) / 1e9
+
+    log("per-kernel timing")
+    kt = kernel_times(rot, 256)
+    d = rot.layers[0].desc(cfg.M)
+    first = moe.moe_ffn_kernel_name(d, 0)
+    dom = first if first != "align_kernel" else moe.moe_ffn_kernel_name(d, 1)
+    # Algorithmic bytes of the gate/up kernel: the packed W13 (values, scales,
+    # zeros) of every touched expert, read once.
+    achieved = touched * b13 / (kt[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": dom, "kernel_us": round(kt[dom] * 1e3, 3),
+                "kernel_times_us": {k: round(v * 1e3, 3) for k, v in kt.items()}}
+
+    extra = {}
+    if not args.no_extra:
+        for name in ("batch_m21", "batch_m256_zipf"):
+            log("context workload", name)
+            r2 = Rotation(name, 8, 16)
+            extra[name] = {k: (round(v, 4) if isinstance(v, float) else v)
+                           for k, v in layer_numbers(r2, 64).items()}
+            del r2
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(rot, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer tokens/s and effective weight GB/s at M=1/21/256; % HBM/MFMA peak",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; int4 weights drawn uniformly, bf16 N(0,1) activations, softmax top-k routing)",
+        "config": {"workload": f"{cfg.name}: M={cfg.M} H={cfg.H} I={cfg.I} E={cfg.E} top-{cfg.k} "
+                               f"int4 AWQ g{cfg.g}, cold weights ({N_LAYER_COPIES} layer copies x "
+                               f"{N_ROUTINGS} routings rotated)",
+                   "M": cfg.M, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "group": cfg.g,
+                   "path": "decode" if moe.moe_ffn_kernel_count(d) == 2 else "grouped",
+                   "parallelism": "single GPU"},
+        "effective_weight_GBps": round(layer_gbps, 1),
+        "hbm_frac_layer": round(layer_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "other_workloads": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,6 +44,10 @@
 extern "C" {
 #endif
 
+#ifndef MOE_API
+#define MOE_API __attribute__((visibility("default")))
+#endif
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent sizes */
@@ -54,7 +58,9 @@ typedef enum {
 } moe_status;
 
 typedef enum {
-  MOE_W_INT4_AWQ = 0,  /* q: uint32 [E][N][K/8], element kk in bits 4*(kk%8)..+3;
+  MOE_W_INT4_AWQ = 0,  /* q: uint32 [E][N][K/8]; word kk/8 holds elements 8*(kk/8)..+7
+                          in AWQ's interleaved order: nibble slot i (bits 4i..4i+3)
+                          holds element [0,2,4,6,1,3,5,7][i];
                           scale: fp16 [E][N][K/group]; zero: uint8 [E][N][K/group] in 0..15;
                           w = (q - zero) * scale */
   MOE_W_MXFP8 = 1      /* q: uint8 OCP E4M3FN [E][N][K]; scale: uint8 E8M0 [E][N][K/32];
@@ -95,7 +101,7 @@ typedef struct {
 /* Number of int32 entries sorted_route_ids needs: roundup(M*k + min(E, M*k)*(b-1), b).
  * expert_block_ids needs capacity / b entries. Host-only and pure; returns 0 when
  * M < 0, k < 1, E < 1 or b < 1. */
-size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
+MOE_API size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
 
 /* Step (1), route alignment ("Route-Block Membership Selects Packed-AWQ
  * Arithmetic": first paragraph; A_e / B(e,j) paragraph; stable-construction
@@ -109,14 +115,14 @@ size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
  * Runs as one workgroup (M*k up to 2^24 routes, E <= 2048).
  * Errors: MOE_ERR_INVALID_ARG (null pointers, M < 0, k < 1, E < 1, b < 1),
  * MOE_ERR_UNSUPPORTED (E > 2048 or M*k > 2^24), MOE_ERR_CAPACITY (capacity too small). */
-moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
+MOE_API moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
                      int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
                      size_t capacity, hipStream_t stream);
 
 /* Bytes of device workspace moe_ffn_forward needs for this description (path
  * resolved as moe_ffn_forward resolves it). Errors as moe_ffn_forward's
  * validation. */
-moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes);
+MOE_API moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes);
 
 /* Steps (1)-(4): y = sum_j w[t,j] * W2[e] (silu(W13g[e] x_t) * W13u[e] x_t).
  *   x         [M][H] bf16 bit patterns
@@ -126,19 +132,21 @@ moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes);
  *   ws        workspace of at least moe_ffn_workspace_size bytes, 256-byte aligned
  * The decode path needs no alignment (the output-stationary design of the
  * warp-decode write-up, "Eliminación del relleno"); the grouped path runs
- * moe_align into the workspace first. The fp32 route-indexed intermediate
- * silu(gate)*up [M*k][I] is left in the workspace at moe_ffn_intermediate_offset.
+ * moe_align into the workspace first. The route-indexed intermediate
+ * silu(gate)*up is left in the workspace (see moe_ffn_intermediate).
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
-moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+MOE_API moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
                            const float* topk_w, float* y, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
-/* Grouped path on a caller-supplied alignment (same layout and meaning as
- * moe_align's outputs, with the given capacity). Lets a caller reorder routes
- * within an expert's rows: the output bytes must not change. Route entries
+/* Grouped path (whatever d->path says) on a caller-supplied alignment (same
+ * layout and meaning as moe_align's outputs, with the given capacity). Lets a
+ * caller reorder routes within an expert's rows: the output bytes must not
+ * change. Route entries
  * outside [0, M*k) are padding; blocks whose expert is outside [0, E) are skipped.
- * Each valid route must appear at most once. Errors as moe_ffn_forward. */
-moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
+ * Each valid route must appear at most once. The workspace must be sized with
+ * d->path = MOE_PATH_GROUPED. Errors as moe_ffn_forward. */
+MOE_API moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
                                    const int32_t* topk_ids, const float* topk_w,
                                    const int32_t* sorted_route_ids,
                                    const int32_t* expert_block_ids,
@@ -148,25 +156,30 @@ moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
 /* Same as moe_ffn_forward, and records events[0] before the first kernel and
  * events[i+1] after kernel i (n_events must be moe_ffn_kernel_count + 1) so a
  * caller can time each kernel on the stream. Events are caller-created. */
-moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
+MOE_API moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
                                     const int32_t* topk_ids, const float* topk_w, float* y,
                                     void* ws, size_t ws_bytes, hipStream_t stream,
                                     hipEvent_t* events, int32_t n_events);
 
 /* Number of kernels moe_ffn_forward launches for this description (0 on error). */
-int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
+MOE_API int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
 
 /* Name of kernel i of moe_ffn_forward for this description, or NULL. */
-const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
+MOE_API const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
 
-/* Byte offset inside the workspace of the fp32 [M*k][I] intermediate. */
-moe_status moe_ffn_intermediate_offset(const moe_ffn_desc* d, size_t* offset);
+/* Where a forward call leaves the route-indexed intermediate silu(gate)*up
+ * inside the workspace (rows of invalid routes are unspecified).
+ *   format 0 (decode path): fp32 [M*k][I] at *offset (*lo_offset == *offset);
+ *   format 1 (grouped path): bf16 hi plane [M*k][I] at *offset and bf16 lo plane
+ *     at *lo_offset, the value being hi + lo (within 2^-17 relative). */
+MOE_API moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* lo_offset,
+                                int32_t* format);
 
 /* Largest M for which MOE_PATH_AUTO picks the decode path. */
-int32_t moe_ffn_auto_decode_max_m(void);
+MOE_API int32_t moe_ffn_auto_decode_max_m(void);
 
 /* Static string for a status code. */
-const char* moe_status_str(moe_status s);
+MOE_API const char* moe_status_str(moe_status s);
 
 #ifdef __cplusplus
 }

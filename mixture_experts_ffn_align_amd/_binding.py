@@ -1,0 +1,211 @@
+"""ctypes binding over libmoe_ffn.so (the C ABI declared in include/moe_ffn.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch supplies device memory and the current stream. If the library has
+not been built this module raises on first use; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_ffn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_ffn.h")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_CAPACITY = 3
+MOE_ERR_WORKSPACE = 4
+MOE_ERR_HIP = 5
+
+MOE_W_INT4_AWQ = 0
+MOE_W_MXFP8 = 1
+
+MOE_PATH_AUTO = 0
+MOE_PATH_DECODE = 1
+MOE_PATH_GROUPED = 2
+
+_c_i32 = ctypes.c_int32
+_c_size = ctypes.c_size_t
+_c_ptr = ctypes.c_void_p
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [("fmt", _c_i32), ("group", _c_i32), ("q", _c_ptr), ("scale", _c_ptr),
+                ("zero", _c_ptr)]
+
+
+class moe_ffn_desc(ctypes.Structure):
+    _fields_ = [("M", _c_i32), ("H", _c_i32), ("I", _c_i32), ("E", _c_i32), ("k", _c_i32),
+                ("b", _c_i32), ("w13", moe_weights), ("w2", moe_weights), ("path", _c_i32),
+                ("max_workgroups", _c_i32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+_SIGNATURES = {
+    "moe_align_capacity": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "moe_align": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr,
+                           _c_size, _c_ptr]),
+    "moe_ffn_workspace_size": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size)]),
+    "moe_ffn_forward": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                 _c_ptr, _c_size, _c_ptr]),
+    "moe_ffn_forward_aligned": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr,
+                                         _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr,
+                                         _c_size, _c_ptr]),
+    "moe_ffn_forward_profiled": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr,
+                                          _c_ptr, _c_ptr, _c_size, _c_ptr,
+                                          ctypes.POINTER(_c_ptr), _c_i32]),
+    "moe_ffn_kernel_count": (_c_i32, [ctypes.POINTER(moe_ffn_desc)]),
+    "moe_ffn_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(moe_ffn_desc), _c_i32]),
+    "moe_ffn_intermediate": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size),
+                                      ctypes.POINTER(_c_size), ctypes.POINTER(_c_i32)]),
+    "moe_ffn_auto_decode_max_m": (_c_i32, []),
+    "moe_status_str": (ctypes.c_char_p, [_c_i32]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixture_experts_ffn_align_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Entry points include/moe_ffn.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def moe_align_capacity(M: int, k: int, E: int, b: int) -> int:
+    return int(lib().moe_align_capacity(M, k, E, b))
+
+
+def moe_align(topk_ids, E: int, b: int, sorted_route_ids, expert_block_ids, num_padded,
+              stream=None, check: bool = True) -> int:
+    M, k = topk_ids.shape
+    st = lib().moe_align(_ptr(topk_ids), M, k, E, b, _ptr(sorted_route_ids),
+                         _ptr(expert_block_ids), _ptr(num_padded),
+                         sorted_route_ids.numel(), _stream(stream))
+    if check:
+        _check(st, "moe_align")
+    return st
+
+
+def weights_struct(fmt: int, group: int, q, scale, zero) -> moe_weights:
+    return moe_weights(fmt, group, _ptr(q), _ptr(scale), _ptr(zero))
+
+
+def make_desc(M: int, H: int, I: int, E: int, k: int, b: int, w13: moe_weights,
+              w2: moe_weights, path: int = MOE_PATH_AUTO, max_workgroups: int = 0) -> moe_ffn_desc:
+    return moe_ffn_desc(M, H, I, E, k, b, w13, w2, path, max_workgroups)
+
+
+def moe_ffn_workspace_size(desc: moe_ffn_desc, check: bool = True):
+    n = _c_size(0)
+    st = lib().moe_ffn_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if check:
+        _check(st, "moe_ffn_workspace_size")
+        return int(n.value)
+    return st, int(n.value)
+
+
+def moe_ffn_forward(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, stream=None,
+                    check: bool = True) -> int:
+    st = lib().moe_ffn_forward(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
+                               _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream))
+    if check:
+        _check(st, "moe_ffn_forward")
+    return st
+
+
+def moe_ffn_forward_aligned(desc: moe_ffn_desc, x, topk_ids, topk_w, sorted_route_ids,
+                            expert_block_ids, num_padded, y, ws, stream=None,
+                            check: bool = True) -> int:
+    st = lib().moe_ffn_forward_aligned(
+        ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(sorted_route_ids),
+        _ptr(expert_block_ids), _ptr(num_padded), sorted_route_ids.numel(), _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    if check:
+        _check(st, "moe_ffn_forward_aligned")
+    return st
+
+
+def moe_ffn_forward_profiled(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, events,
+                             stream=None) -> None:
+    """``events`` are torch.cuda.Event(enable_timing=True) objects, one more than
+    the kernel count; they are recorded around every kernel on the stream."""
+    for e in events:
+        if int(e.cuda_event) == 0:   # torch creates the HIP event on first record
+            e.record()
+    handles = (_c_ptr * len(events))(*[int(e.cuda_event) for e in events])
+    st = lib().moe_ffn_forward_profiled(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream), handles, len(events))
+    _check(st, "moe_ffn_forward_profiled")
+
+
+def moe_ffn_kernel_count(desc: moe_ffn_desc) -> int:
+    return int(lib().moe_ffn_kernel_count(ctypes.byref(desc)))
+
+
+def moe_ffn_kernel_name(desc: moe_ffn_desc, i: int) -> str | None:
+    r = lib().moe_ffn_kernel_name(ctypes.byref(desc), i)
+    return None if r is None else r.decode()
+
+
+def moe_ffn_intermediate(desc: moe_ffn_desc) -> tuple[int, int, int]:
+    off, lo, fmt = _c_size(0), _c_size(0), _c_i32(0)
+    _check(lib().moe_ffn_intermediate(ctypes.byref(desc), ctypes.byref(off), ctypes.byref(lo),
+                                      ctypes.byref(fmt)), "moe_ffn_intermediate")
+    return int(off.value), int(lo.value), int(fmt.value)
+
+
+def moe_ffn_auto_decode_max_m() -> int:
+    return int(lib().moe_ffn_auto_decode_max_m())

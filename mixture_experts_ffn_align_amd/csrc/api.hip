@@ -1,0 +1,284 @@
+// C ABI of the MoE expert-FFN library: argument validation, workspace layout,
+// path selection and kernel launches. Nothing here allocates device memory or
+// synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "moe_ffn.h"
+
+namespace {
+
+constexpr int32_t kMaxExperts = 2048;
+constexpr int64_t kMaxRoutes = int64_t(1) << 24;
+constexpr int32_t kAutoDecodeMaxM = 16;
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t capacity_of(int64_t M, int64_t k, int64_t E, int64_t b) {
+  const int64_t mk = M * k;
+  const int64_t raw = mk + (E < mk ? E : mk) * (b - 1);
+  return static_cast<size_t>((raw + b - 1) / b * b);
+}
+
+struct Layout {
+  int path = MOE_PATH_DECODE;
+  size_t cap = 0;        // alignment capacity (grouped)
+  size_t off_sorted = 0, off_blocks = 0, off_npad = 0;
+  size_t off_a = 0, off_a_lo = 0, off_yhat = 0;
+  size_t total = 0;
+};
+
+bool weights_ok(const moe_weights& w) {
+  if (w.q == nullptr || w.scale == nullptr || w.group <= 0) return false;
+  if (!aligned(w.q, 16)) return false;
+  if (w.fmt == MOE_W_INT4_AWQ && w.zero == nullptr) return false;
+  return true;
+}
+
+moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
+  if (d == nullptr) return MOE_ERR_INVALID_ARG;
+  if (d->M < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->b < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GROUPED) return MOE_ERR_INVALID_ARG;
+  if (d->max_workgroups < 0) return MOE_ERR_INVALID_ARG;
+  if (d->w13.fmt != d->w2.fmt) return MOE_ERR_INVALID_ARG;
+  if (d->w13.fmt != MOE_W_INT4_AWQ && d->w13.fmt != MOE_W_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(d->w13) || !weights_ok(d->w2)) return MOE_ERR_INVALID_ARG;
+  if ((d->H % 32) != 0 || (d->I % 32) != 0) return MOE_ERR_INVALID_ARG;
+  if ((d->H % d->w13.group) != 0 || (d->I % d->w2.group) != 0) return MOE_ERR_INVALID_ARG;
+  if ((d->w13.group % 32) != 0 || (d->w2.group % 32) != 0) return MOE_ERR_INVALID_ARG;
+  if (d->w13.fmt == MOE_W_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (d->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  const int64_t mk = int64_t(d->M) * d->k;
+  if (mk > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+
+  int path = d->path;
+  if (path == MOE_PATH_AUTO) path = d->M <= kAutoDecodeMaxM ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
+  if (need_align_buffers) path = MOE_PATH_GROUPED;
+  L->path = path;
+  if (path == MOE_PATH_DECODE) {
+    if (!moe::decode_shape_ok(d->H, d->I, d->k)) return MOE_ERR_UNSUPPORTED;
+    L->off_a = 0;
+    L->total = round256(size_t(mk) * d->I * sizeof(float));
+    if (L->total == 0) L->total = 256;
+    return MOE_OK;
+  }
+  if (!moe::grouped_shape_ok(d->H, d->I, d->b, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
+  L->cap = capacity_of(d->M, d->k, d->E, d->b);
+  size_t o = 0;
+  L->off_sorted = o; o += round256(L->cap * sizeof(int32_t));
+  L->off_blocks = o; o += round256((L->cap / d->b) * sizeof(int32_t));
+  L->off_npad = o;   o += 256;
+  L->off_a = o;      o += round256(size_t(mk) * d->I * sizeof(uint16_t));
+  L->off_a_lo = o;   o += round256(size_t(mk) * d->I * sizeof(uint16_t));
+  L->off_yhat = o;   o += round256(size_t(mk) * d->H * sizeof(float));
+  L->total = o;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Enqueues the kernels of one forward call. `align_src` is null for the
+// normal path (alignment computed into the workspace) or the caller's
+// alignment for moe_ffn_forward_aligned. Events, when given, bracket every
+// kernel.
+moe_status run_forward(const moe_ffn_desc* d, const Layout& L, const uint16_t* x,
+                       const int32_t* ids, const float* w, float* y, void* ws,
+                       const int32_t* a_sorted, const int32_t* a_blocks, const int32_t* a_npad,
+                       size_t a_cap, hipStream_t s, hipEvent_t* ev) {
+  int kidx = 0;
+  auto mark = [&](void) -> moe_status {
+    if (ev != nullptr && hipEventRecord(ev[kidx], s) != hipSuccess) return MOE_ERR_HIP;
+    ++kidx;
+    return MOE_OK;
+  };
+  moe_status st;
+  if ((st = mark()) != MOE_OK) return st;
+  if (L.path == MOE_PATH_DECODE) {
+    moe::DecodeArgs p{};
+    p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
+    p.a = at<float>(ws, L.off_a); p.y = y;
+    p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k;
+    p.max_workgroups = d->max_workgroups;
+    if ((st = hip_status(moe::launch_decode_gate_up(p, s))) != MOE_OK) return st;
+    if ((st = mark()) != MOE_OK) return st;
+    if ((st = hip_status(moe::launch_decode_down(p, s))) != MOE_OK) return st;
+    return mark();
+  }
+  moe::GroupedArgs p{};
+  const int64_t mk = int64_t(d->M) * d->k;
+  p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
+  p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_a_lo);
+  p.yhat = at<float>(ws, L.off_yhat); p.y = y;
+  p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k; p.b = d->b;
+  p.max_workgroups = d->max_workgroups;
+  if (a_sorted == nullptr) {
+    p.sorted = at<int32_t>(ws, L.off_sorted);
+    p.blocks = at<int32_t>(ws, L.off_blocks);
+    p.num_padded = at<int32_t>(ws, L.off_npad);
+    p.nblk = static_cast<int>(L.cap / d->b);
+    if ((st = hip_status(moe::launch_align(ids, static_cast<int>(mk), d->E, d->b,
+                                           at<int32_t>(ws, L.off_sorted), at<int32_t>(ws, L.off_blocks),
+                                           at<int32_t>(ws, L.off_npad), static_cast<int>(L.cap), s))) != MOE_OK)
+      return st;
+    if ((st = mark()) != MOE_OK) return st;
+  } else {
+    p.sorted = a_sorted; p.blocks = a_blocks; p.num_padded = a_npad;
+    p.nblk = static_cast<int>(a_cap / d->b);
+  }
+  if ((st = hip_status(moe::launch_grouped_gate_up(p, s))) != MOE_OK) return st;
+  if ((st = mark()) != MOE_OK) return st;
+  if ((st = hip_status(moe::launch_grouped_down(p, s))) != MOE_OK) return st;
+  if ((st = mark()) != MOE_OK) return st;
+  if ((st = hip_status(moe::launch_combine(p, s))) != MOE_OK) return st;
+  return mark();
+}
+
+moe_status check_io(const moe_ffn_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
+                    float* y, void* ws, size_t ws_bytes, const Layout& L) {
+  if (x == nullptr || ids == nullptr || w == nullptr || y == nullptr || ws == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || !aligned(ids, 4) || !aligned(w, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  (void)d;
+  return MOE_OK;
+}
+
+int kernel_count_of(const Layout& L, bool aligned_input) {
+  if (L.path == MOE_PATH_DECODE) return 2;
+  return aligned_input ? 3 : 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b) {
+  if (M < 0 || k < 1 || E < 1 || b < 1) return 0;
+  return capacity_of(M, k, E, b);
+}
+
+moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
+                     int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
+                     size_t capacity, hipStream_t stream) {
+  if (M < 0 || k < 1 || E < 1 || b < 1) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (topk_ids == nullptr || sorted_route_ids == nullptr || expert_block_ids == nullptr ||
+      num_padded == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || int64_t(M) * k > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+  const size_t need = capacity_of(M, k, E, b);
+  if (capacity < need) return MOE_ERR_CAPACITY;
+  if (capacity > size_t(INT32_MAX)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_align(topk_ids, M * k, E, b, sorted_route_ids, expert_block_ids,
+                                      num_padded, static_cast<int>(capacity), stream));
+}
+
+moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  Layout L;
+  const moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                           const float* topk_w, float* y, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  Layout L;
+  moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
+  return run_forward(d, L, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0, stream, nullptr);
+}
+
+moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
+                                   const int32_t* topk_ids, const float* topk_w,
+                                   const int32_t* sorted_route_ids,
+                                   const int32_t* expert_block_ids,
+                                   const int32_t* num_padded, size_t capacity, float* y,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moe_status st = validate(d, &L, true);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
+  if (sorted_route_ids == nullptr || expert_block_ids == nullptr || num_padded == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (capacity % size_t(d->b) != 0 || capacity > size_t(INT32_MAX)) return MOE_ERR_INVALID_ARG;
+  if (capacity < capacity_of(d->M, d->k, d->E, d->b)) return MOE_ERR_CAPACITY;
+  return run_forward(d, L, x, topk_ids, topk_w, y, ws, sorted_route_ids, expert_block_ids,
+                     num_padded, capacity, stream, nullptr);
+}
+
+moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
+                                    const int32_t* topk_ids, const float* topk_w, float* y,
+                                    void* ws, size_t ws_bytes, hipStream_t stream,
+                                    hipEvent_t* events, int32_t n_events) {
+  Layout L;
+  moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
+  if (events == nullptr || n_events != kernel_count_of(L, false) + 1) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+  return run_forward(d, L, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0, stream, events);
+}
+
+int32_t moe_ffn_kernel_count(const moe_ffn_desc* d) {
+  Layout L;
+  if (validate(d, &L, false) != MOE_OK) return 0;
+  return kernel_count_of(L, false);
+}
+
+const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i) {
+  Layout L;
+  if (validate(d, &L, false) != MOE_OK) return nullptr;
+  static const char* const kDecode[] = {"decode_gate_up_int4", "decode_down_int4"};
+  static const char* const kGrouped[] = {"align_kernel", "grouped_gate_up_int4", "grouped_down_int4",
+                                         "combine_topk"};
+  if (L.path == MOE_PATH_DECODE) return (i >= 0 && i < 2) ? kDecode[i] : nullptr;
+  return (i >= 0 && i < 4) ? kGrouped[i] : nullptr;
+}
+
+moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* lo_offset,
+                                int32_t* format) {
+  if (offset == nullptr || lo_offset == nullptr || format == nullptr) return MOE_ERR_INVALID_ARG;
+  Layout L;
+  const moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  *offset = L.off_a;
+  *lo_offset = L.path == MOE_PATH_DECODE ? L.off_a : L.off_a_lo;
+  *format = L.path == MOE_PATH_DECODE ? 0 : 1;
+  return MOE_OK;
+}
+
+int32_t moe_ffn_auto_decode_max_m(void) { return kAutoDecodeMaxM; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, format or path";
+    case MOE_ERR_CAPACITY: return "alignment capacity too small";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -9,6 +9,14 @@ namespace moe {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of weights that are read once: marked nontemporal
+// so they do not displace reused data (activations, intermediates) in cache.
+__device__ __forceinline__ uint4 load_stream16(const uint32_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 constexpr int kWave = 64;
 
@@ -20,9 +28,13 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Eight int4 values of one word, biased by 128, as four bf16 pairs:
-// pair i = (128 + q_i, 128 + q_{i+4}). 0x4300 is bf16 128.0 with a zero
-// mantissa, so OR-ing a 4-bit value into the mantissa gives 128 + q exactly.
+// Eight int4 values of one word, biased by 128, as four bf16 pairs. Words
+// use AWQ's interleaved nibble order (slot i holds element [0,2,4,6,1,3,5,7][i]),
+// so (w >> 4i) & 0x000F000F puts elements 2i and 2i+1 in the low and high
+// halves: pair i = (128 + q_{2i}, 128 + q_{2i+1}), the same element order as
+// word i of eight consecutive bf16 activations. 0x4300 is bf16 128.0 with a
+// zero mantissa, so OR-ing a 4-bit value into the mantissa gives 128 + q
+// exactly.
 __device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t p[4]) {
   const uint32_t m = 0x000F000Fu, c = 0x43004300u;
   p[0] = (w & m) | c;
@@ -31,14 +43,18 @@ __device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t p[4]) {
   p[3] = ((w >> 12) & m) | c;
 }
 
-// Eight consecutive bf16 activations (four words, element 2i in the low
-// half of word i) regrouped into the pairs (x_i, x_{i+4}) that match
-// unpack8_bias128.
-__device__ __forceinline__ void pair_x8(const uint32_t x[4], uint32_t p[4]) {
-  p[0] = (x[0] & 0xFFFFu) | (x[2] << 16);
-  p[1] = (x[0] >> 16) | (x[2] & 0xFFFF0000u);
-  p[2] = (x[1] & 0xFFFFu) | (x[3] << 16);
-  p[3] = (x[1] >> 16) | (x[3] & 0xFFFF0000u);
+// The eight int4 values of one word as fp32, in element order.
+__device__ __forceinline__ void unpack8_f32(uint32_t w, float q[8]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // slots 0,2,4,6 -> elements 0,4,1,5
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // slots 1,3,5,7 -> elements 2,6,3,7
+  q[0] = (float)(lo & 0xFF);
+  q[4] = (float)((lo >> 8) & 0xFF);
+  q[1] = (float)((lo >> 16) & 0xFF);
+  q[5] = (float)(lo >> 24);
+  q[2] = (float)(hi & 0xFF);
+  q[6] = (float)((hi >> 8) & 0xFF);
+  q[3] = (float)((hi >> 16) & 0xFF);
+  q[7] = (float)(hi >> 24);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_ffn.h"
+
+namespace moe {
+
+// Route alignment (align.hip).
+size_t align_lds_bytes(int E);
+hipError_t launch_align(const int32_t* ids, int mk, int E, int b, int32_t* sorted, int32_t* blocks,
+                        int32_t* num_padded, int cap, hipStream_t stream);
+
+// Decode path (decode.hip).
+struct DecodeArgs {
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* topk_w;
+  moe_weights w13, w2;
+  float* a;  // fp32 [M*k][I]
+  float* y;  // fp32 [M][H]
+  int M, H, I, E, k;
+  int max_workgroups;
+};
+bool decode_shape_ok(int H, int I, int k);
+hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream);
+hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream);
+
+// Grouped path (grouped.hip).
+struct GroupedArgs {
+  const uint16_t* x;
+  const int32_t* ids;
+  const float* topk_w;
+  const int32_t* sorted;
+  const int32_t* blocks;
+  const int32_t* num_padded;
+  moe_weights w13, w2;
+  uint16_t* a_hi;  // bf16 [M*k][I]
+  uint16_t* a_lo;  // bf16 [M*k][I]
+  float* yhat;     // fp32 [M*k][H]
+  float* y;        // fp32 [M][H]
+  int M, H, I, E, k, b;
+  int nblk;        // blocks in the alignment buffers (capacity / b)
+  int max_workgroups;
+};
+bool grouped_shape_ok(int H, int I, int b, int g13, int g2);
+hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream);
+hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream);
+hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream);
+
+}  // namespace moe

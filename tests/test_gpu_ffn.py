@@ -1,0 +1,134 @@
+"""GPU layer output vs the fp64 oracle, per path, plus edge cases.
+
+Tolerance (the layer's stated bar): rel-L2 <= 1e-3 and max-abs <= 1e-2 *
+rms(oracle). The intermediate silu(gate)*up is also compared, which localises
+a failure to the gate/up or the down/combine stage.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_align_amd as moe
+import oracle
+from tests._checks import ffn_errors, ffn_mismatch
+from workloads import CONFIGS, make_workload
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"decode": moe.MOE_PATH_DECODE, "grouped": moe.MOE_PATH_GROUPED}
+
+
+def _gpu():
+    from tests import _gpu
+    return _gpu
+
+
+def _check_intermediate(dw, st, path):
+    a = dw.intermediate(path)
+    valid = (dw.wl.topk_ids.reshape(-1) >= 0) & (dw.wl.topk_ids.reshape(-1) < dw.cfg.E)
+    err = ffn_errors(a[valid], st["a"][valid])
+    assert err["rel_l2"] < 1e-4, err
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_m1", "batch_m21", "batch_m256_zipf"])
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_ffn_parity_full_size(name, path):
+    g = _gpu()
+    dw = g.device_workload(name)
+    st = g.oracle_stages(name)
+    g.announce("ffn", name, path)
+    y = dw.forward(PATHS[path]).cpu().numpy()
+    err = ffn_errors(y, st["y"])
+    print(name, path, err)
+    assert ffn_mismatch(y, st["y"]) is None, err
+    _check_intermediate(dw, st, PATHS[path])
+
+
+def _custom(seed, **kw):
+    cfg = dataclasses.replace(CONFIGS["tiny"], name="custom", **kw)
+    return make_workload(cfg, seed=seed)
+
+
+RAGGED = [
+    dict(M=1, H=256, I=128, E=8, k=2, b=8, g=64),
+    dict(M=3, H=512, I=160, E=16, k=4, b=16, g=32),      # I not a multiple of 64 -> decode only
+    dict(M=37, H=256, I=128, E=8, k=2, b=16, g=128),
+    dict(M=70, H=1024, I=256, E=32, k=6, b=32, g=128),
+    dict(M=9, H=2048, I=768, E=128, k=8, b=64, g=128),
+    dict(M=5, H=256, I=128, E=1, k=1, b=8, g=32),
+    dict(M=20, H=384, I=2176, E=4, k=2, b=8, g=128),     # I/32 = 68 chunks > 64 lanes
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "M{M}_H{H}_I{I}_E{E}_k{k}_b{b}_g{g}".format(**s))
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_ffn_parity_ragged(shape, path):
+    g = _gpu()
+    wl = _custom(11, **shape)
+    dw = g.DeviceWorkload(wl)
+    d = dw.layer.desc(wl.cfg.M, PATHS[path])
+    st_code, _ = moe.moe_ffn_workspace_size(d, check=False)
+    if st_code == moe.MOE_ERR_UNSUPPORTED:
+        pytest.skip("shape not supported on this path")
+    ref = oracle.ffn_stages(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
+    g.announce("ffn-ragged", shape, path)
+    y = dw.forward(PATHS[path]).cpu().numpy()
+    assert ffn_mismatch(y, ref["y"]) is None, ffn_errors(y, ref["y"])
+    _check_intermediate(dw, ref, PATHS[path])
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_ffn_invalid_ids_are_skipped(path):
+    g = _gpu()
+    wl = _custom(12, M=6, H=256, I=128, E=8, k=3, b=8, g=64)
+    wl.topk_ids[0, 1] = -1
+    wl.topk_ids[2, 0] = 8
+    wl.topk_ids[5, :] = -3          # a token with no valid route -> y row is zero
+    dw = g.DeviceWorkload(wl)
+    ref = oracle.ffn(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
+    g.announce("ffn-invalid", path)
+    y = dw.forward(PATHS[path]).cpu().numpy()
+    assert ffn_mismatch(y, ref) is None, ffn_errors(y, ref)
+    assert np.all(y[5] == 0.0)
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_ffn_zero_input_gives_exact_zero(path):
+    g = _gpu()
+    dw = g.device_workload("batch_m21")
+    x0 = torch.zeros_like(dw.x)
+    g.announce("ffn-zero", path)
+    y = dw.forward(PATHS[path], x=x0)
+    assert bool(torch.all(y == 0.0))
+
+
+def test_ffn_m0_is_noop():
+    g = _gpu()
+    dw = g.device_workload("tiny")
+    y = torch.full((0, dw.cfg.H), 1.0, device="cuda")
+    dw.layer.forward(dw.x[:0], dw.ids[:0], dw.w[:0], y=y)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_ffn_identical_experts_is_dense_swiglu(path):
+    # All experts equal and w = 1/k: y equals one dense SwiGLU, computed with
+    # torch float64 on the CPU from the oracle's dequantised weights.
+    g = _gpu()
+    wl = make_workload("batch_m21", seed=3)
+    for pw in (wl.w13, wl.w2):
+        pw.q[:] = pw.q[:1]
+        pw.s[:] = pw.s[:1]
+        pw.z[:] = pw.z[:1]
+    wl.topk_w[:] = 1.0 / wl.cfg.k
+    dw = g.DeviceWorkload(wl)
+    I = wl.cfg.I
+    W13 = torch.from_numpy(oracle.dequant_int4(wl.w13.q[0], wl.w13.s[0], wl.w13.z[0], wl.w13.g))
+    W2 = torch.from_numpy(oracle.dequant_int4(wl.w2.q[0], wl.w2.s[0], wl.w2.z[0], wl.w2.g))
+    x = torch.from_numpy(oracle.bf16_to_f64(wl.x))
+    ref = (torch.nn.functional.silu(x @ W13[:I].T) * (x @ W13[I:].T)) @ W2.T
+    g.announce("ffn-identical", path)
+    y = dw.forward(PATHS[path]).cpu().numpy()
+    assert ffn_mismatch(y, ref.numpy()) is None
