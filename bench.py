@@ -138,23 +138,45 @@ def time_graph(rot, steps, warmup):
     return t0.elapsed_time(t1)
 
 
-def kernel_times(rot, steps):
-    """Average duration (ms) of each kernel of the layer, from events recorded
-    around every kernel on the launch stream, over `steps` eager calls."""
+def stage_times(rot, steps):
+    """Average duration (us) of each stage of the layer, each replayed alone
+    from a HIP graph over the same rotation (moe_ffn_gate_up, then
+    moe_ffn_down_combine). On the decode path each stage is exactly one
+    kernel, so this is the per-kernel duration a kernel trace reports."""
     import torch
     import mixture_experts_ffn_align_amd as moe
-    d = rot.layers[0].desc(rot.cfg.M)
-    nk = moe.moe_ffn_kernel_count(d)
-    names = [moe.moe_ffn_kernel_name(d, i) for i in range(nk)]
-    sums = np.zeros(nk)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
-    for i in range(steps):
-        rot.step(i, profiled_events=evs[i])
-    torch.cuda.synchronize()
-    for i in range(steps):
-        for j in range(nk):
-            sums[j] += evs[i][j].elapsed_time(evs[i][j + 1])
-    return dict(zip(names, (sums / steps).tolist()))
+
+    def gate_up(i):
+        layer = rot.layers[i % len(rot.layers)]
+        x, ids, _ = rot.inputs[i % len(rot.inputs)]
+        moe.moe_ffn_gate_up(layer.desc(rot.cfg.M), x, ids, rot.ws)
+
+    def down(i):
+        layer = rot.layers[i % len(rot.layers)]
+        _, ids, w = rot.inputs[i % len(rot.inputs)]
+        moe.moe_ffn_down_combine(layer.desc(rot.cfg.M), ids, w, rot.y, rot.ws)
+
+    out = {}
+    for name, fn in (("gate_up", gate_up), ("down_combine", down)):
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        out[name] = t0.elapsed_time(t1) * 1e3 / steps
+    return out
 
 
 def cpu_baseline(rot, seconds):
@@ -226,18 +248,23 @@ def main():
     touched = float(np.mean([rot.touched[i % N_ROUTINGS] for i in range(args.steps)]))
     layer_gbps = touched * per_expert / (t_step * 1e-3) / 1e9
 
-    log("per-kernel timing")
-    kt = kernel_times(rot, 256)
+    log("per-stage timing")
+    st_us = stage_times(rot, 512)
     d = rot.layers[0].desc(cfg.M)
-    first = moe.moe_ffn_kernel_name(d, 0)
-    dom = first if first != "align_kernel" else moe.moe_ffn_kernel_name(d, 1)
-    # Algorithmic bytes of the gate/up kernel: the packed W13 (values, scales,
-    # zeros) of every touched expert, read once.
-    achieved = touched * b13 / (kt[dom] * 1e-3) / 1e9
+    path = "decode" if moe.moe_ffn_kernel_count(d) == 2 else "grouped"
+    # Algorithmic bytes of a stage: the packed weights (values, scales, zeros)
+    # of every touched expert for that projection, each read once.
+    stage_bytes = {"gate_up": touched * b13, "down_combine": touched * b2}
+    dom = max(st_us, key=st_us.get)
+    names = {"gate_up": moe.moe_ffn_kernel_name(d, 0 if path == "decode" else 1),
+             "down_combine": moe.moe_ffn_kernel_name(d, 1 if path == "decode" else 2)}
+    achieved = stage_bytes[dom] / (st_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": dom, "kernel_us": round(kt[dom] * 1e3, 3),
-                "kernel_times_us": {k: round(v * 1e3, 3) for k, v in kt.items()}}
+                "kernel": names[dom], "kernel_us": round(st_us[dom], 3),
+                "algorithmic_bytes": int(stage_bytes[dom]),
+                "stage_us": {k: round(v, 3) for k, v in st_us.items()},
+                "stage_GBps": {k: round(stage_bytes[k] / (v * 1e-6) / 1e9, 1) for k, v in st_us.items()}}
 
     extra = {}
     if not args.no_extra:
@@ -271,7 +298,7 @@ def main():
                                f"int4 AWQ g{cfg.g}, cold weights ({N_LAYER_COPIES} layer copies x "
                                f"{N_ROUTINGS} routings rotated)",
                    "M": cfg.M, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "group": cfg.g,
-                   "path": "decode" if moe.moe_ffn_kernel_count(d) == 2 else "grouped",
+                   "path": path,
                    "parallelism": "single GPU"},
         "effective_weight_GBps": round(layer_gbps, 1),
         "hbm_frac_layer": round(layer_gbps / HBM_PEAK_GBPS, 4),

@@ -161,6 +161,22 @@ MOE_API moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_
                                     void* ws, size_t ws_bytes, hipStream_t stream,
                                     hipEvent_t* events, int32_t n_events);
 
+/* Step (2) alone (preceded by step (1) on the grouped path): enqueues the
+ * kernels of moe_ffn_forward up to the intermediate silu(gate)*up, which is
+ * left in the workspace (see moe_ffn_intermediate). Lets a caller inspect or
+ * time the stages separately. Arguments and errors as moe_ffn_forward. */
+MOE_API moe_status moe_ffn_gate_up(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps (3)-(4) alone: the down projection and the top-k combine, reading the
+ * intermediate (and, on the grouped path, the alignment) that a preceding
+ * moe_ffn_gate_up call with the same description and topk_ids left in ws.
+ * moe_ffn_gate_up followed by moe_ffn_down_combine gives the same bytes as
+ * moe_ffn_forward. Arguments and errors as moe_ffn_forward. */
+MOE_API moe_status moe_ffn_down_combine(const moe_ffn_desc* d, const int32_t* topk_ids,
+                                        const float* topk_w, float* y, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
 /* Number of kernels moe_ffn_forward launches for this description (0 on error). */
 MOE_API int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
 

@@ -23,9 +23,11 @@ from ._binding import (  # noqa: F401
     moe_align_capacity,
     moe_ffn_auto_decode_max_m,
     moe_ffn_desc,
+    moe_ffn_down_combine,
     moe_ffn_forward,
     moe_ffn_forward_aligned,
     moe_ffn_forward_profiled,
+    moe_ffn_gate_up,
     moe_ffn_intermediate,
     moe_ffn_kernel_count,
     moe_ffn_kernel_name,

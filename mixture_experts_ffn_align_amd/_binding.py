@@ -63,6 +63,10 @@ _SIGNATURES = {
     "moe_ffn_forward_profiled": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_ptr, _c_size, _c_ptr,
                                           ctypes.POINTER(_c_ptr), _c_i32]),
+    "moe_ffn_gate_up": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_size,
+                                 _c_ptr]),
+    "moe_ffn_down_combine": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                      _c_size, _c_ptr]),
     "moe_ffn_kernel_count": (_c_i32, [ctypes.POINTER(moe_ffn_desc)]),
     "moe_ffn_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(moe_ffn_desc), _c_i32]),
     "moe_ffn_intermediate": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size),
@@ -189,6 +193,17 @@ def moe_ffn_forward_profiled(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, eve
                                         _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                         _stream(stream), handles, len(events))
     _check(st, "moe_ffn_forward_profiled")
+
+
+def moe_ffn_gate_up(desc: moe_ffn_desc, x, topk_ids, ws, stream=None) -> None:
+    _check(lib().moe_ffn_gate_up(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "moe_ffn_gate_up")
+
+
+def moe_ffn_down_combine(desc: moe_ffn_desc, topk_ids, topk_w, y, ws, stream=None) -> None:
+    _check(lib().moe_ffn_down_combine(ctypes.byref(desc), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
+                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_ffn_down_combine")
 
 
 def moe_ffn_kernel_count(desc: moe_ffn_desc) -> int:

@@ -62,7 +62,7 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (need_align_buffers) path = MOE_PATH_GROUPED;
   L->path = path;
   if (path == MOE_PATH_DECODE) {
-    if (!moe::decode_shape_ok(d->H, d->I, d->k)) return MOE_ERR_UNSUPPORTED;
+    if (!moe::decode_shape_ok(d->H, d->I, d->k, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
     L->off_a = 0;
     L->total = round256(size_t(mk) * d->I * sizeof(float));
     if (L->total == 0) L->total = 256;
@@ -88,11 +88,16 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Enqueues the kernels of one forward call. `align_src` is null for the
+// Stages of one forward call: kStageGateUp = step (2) (with step (1) on the
+// grouped path), kStageDown = steps (3)-(4).
+constexpr int kStageGateUp = 1;
+constexpr int kStageDown = 2;
+
+// Enqueues the kernels of the requested stages. `align_src` is null for the
 // normal path (alignment computed into the workspace) or the caller's
 // alignment for moe_ffn_forward_aligned. Events, when given, bracket every
 // kernel.
-moe_status run_forward(const moe_ffn_desc* d, const Layout& L, const uint16_t* x,
+moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const uint16_t* x,
                        const int32_t* ids, const float* w, float* y, void* ws,
                        const int32_t* a_sorted, const int32_t* a_blocks, const int32_t* a_npad,
                        size_t a_cap, hipStream_t s, hipEvent_t* ev) {
@@ -110,10 +115,15 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, const uint16_t* x
     p.a = at<float>(ws, L.off_a); p.y = y;
     p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k;
     p.max_workgroups = d->max_workgroups;
-    if ((st = hip_status(moe::launch_decode_gate_up(p, s))) != MOE_OK) return st;
-    if ((st = mark()) != MOE_OK) return st;
-    if ((st = hip_status(moe::launch_decode_down(p, s))) != MOE_OK) return st;
-    return mark();
+    if (stages & kStageGateUp) {
+      if ((st = hip_status(moe::launch_decode_gate_up(p, s))) != MOE_OK) return st;
+      if ((st = mark()) != MOE_OK) return st;
+    }
+    if (stages & kStageDown) {
+      if ((st = hip_status(moe::launch_decode_down(p, s))) != MOE_OK) return st;
+      if ((st = mark()) != MOE_OK) return st;
+    }
+    return MOE_OK;
   }
   moe::GroupedArgs p{};
   const int64_t mk = int64_t(d->M) * d->k;
@@ -127,21 +137,28 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, const uint16_t* x
     p.blocks = at<int32_t>(ws, L.off_blocks);
     p.num_padded = at<int32_t>(ws, L.off_npad);
     p.nblk = static_cast<int>(L.cap / d->b);
-    if ((st = hip_status(moe::launch_align(ids, static_cast<int>(mk), d->E, d->b,
-                                           at<int32_t>(ws, L.off_sorted), at<int32_t>(ws, L.off_blocks),
-                                           at<int32_t>(ws, L.off_npad), static_cast<int>(L.cap), s))) != MOE_OK)
-      return st;
-    if ((st = mark()) != MOE_OK) return st;
+    if (stages & kStageGateUp) {
+      if ((st = hip_status(moe::launch_align(ids, static_cast<int>(mk), d->E, d->b,
+                                             at<int32_t>(ws, L.off_sorted), at<int32_t>(ws, L.off_blocks),
+                                             at<int32_t>(ws, L.off_npad), static_cast<int>(L.cap), s))) != MOE_OK)
+        return st;
+      if ((st = mark()) != MOE_OK) return st;
+    }
   } else {
     p.sorted = a_sorted; p.blocks = a_blocks; p.num_padded = a_npad;
     p.nblk = static_cast<int>(a_cap / d->b);
   }
-  if ((st = hip_status(moe::launch_grouped_gate_up(p, s))) != MOE_OK) return st;
-  if ((st = mark()) != MOE_OK) return st;
-  if ((st = hip_status(moe::launch_grouped_down(p, s))) != MOE_OK) return st;
-  if ((st = mark()) != MOE_OK) return st;
-  if ((st = hip_status(moe::launch_combine(p, s))) != MOE_OK) return st;
-  return mark();
+  if (stages & kStageGateUp) {
+    if ((st = hip_status(moe::launch_grouped_gate_up(p, s))) != MOE_OK) return st;
+    if ((st = mark()) != MOE_OK) return st;
+  }
+  if (stages & kStageDown) {
+    if ((st = hip_status(moe::launch_grouped_down(p, s))) != MOE_OK) return st;
+    if ((st = mark()) != MOE_OK) return st;
+    if ((st = hip_status(moe::launch_combine(p, s))) != MOE_OK) return st;
+    if ((st = mark()) != MOE_OK) return st;
+  }
+  return MOE_OK;
 }
 
 moe_status check_io(const moe_ffn_desc* d, const uint16_t* x, const int32_t* ids, const float* w,
@@ -202,7 +219,8 @@ moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32
   if (st != MOE_OK) return st;
   if (d->M == 0) return MOE_OK;
   if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
-  return run_forward(d, L, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0, stream, nullptr);
+  return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,
+                     stream, nullptr);
 }
 
 moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
@@ -220,8 +238,8 @@ moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
     return MOE_ERR_INVALID_ARG;
   if (capacity % size_t(d->b) != 0 || capacity > size_t(INT32_MAX)) return MOE_ERR_INVALID_ARG;
   if (capacity < capacity_of(d->M, d->k, d->E, d->b)) return MOE_ERR_CAPACITY;
-  return run_forward(d, L, x, topk_ids, topk_w, y, ws, sorted_route_ids, expert_block_ids,
-                     num_padded, capacity, stream, nullptr);
+  return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, sorted_route_ids,
+                     expert_block_ids, num_padded, capacity, stream, nullptr);
 }
 
 moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
@@ -236,7 +254,35 @@ moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
   if (events == nullptr || n_events != kernel_count_of(L, false) + 1) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < n_events; ++i)
     if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
-  return run_forward(d, L, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0, stream, events);
+  return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,
+                     stream, events);
+}
+
+moe_status moe_ffn_gate_up(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if (x == nullptr || topk_ids == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(topk_ids, 4)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return run_forward(d, L, kStageGateUp, x, topk_ids, nullptr, nullptr, ws, nullptr, nullptr, nullptr, 0,
+                     stream, nullptr);
+}
+
+moe_status moe_ffn_down_combine(const moe_ffn_desc* d, const int32_t* topk_ids, const float* topk_w,
+                                float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if (topk_ids == nullptr || topk_w == nullptr || y == nullptr || ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(ws, 256) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return run_forward(d, L, kStageDown, nullptr, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,
+                     stream, nullptr);
 }
 
 int32_t moe_ffn_kernel_count(const moe_ffn_desc* d) {

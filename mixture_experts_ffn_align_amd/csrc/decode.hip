@@ -3,22 +3,26 @@
 //
 // No alignment, gather, scatter or per-expert output buffer: each wave64 owns
 // a fixed set of outputs, streams exactly the packed weight rows they need
-// from HBM, reduces across its lanes with a fixed butterfly, and writes each
-// output once.
+// from HBM, reduces across its lanes in a fixed order, and writes each output
+// once.
 //
 // Kernel 1 (gate/up): a wave owns kNpw intermediate neurons of one route
-//   (token t, expert e) and streams their gate and up rows. Lane l covers the
-//   32-element chunks c = l, l+64, ... of the reduction (H). Weights are
-//   unpacked to bf16 (128 + q) pairs and multiplied with the bf16 activation
-//   pairs by v_dot2c_f32_bf16 (exact products, fp32 sums); per chunk the bias
-//   and zero point are removed in fp32: s * (sum x(128+q) - (128+z) sum x).
-//   silu(gate) * up is written to the fp32 intermediate a[r][i].
-// Kernel 2 (down + combine): a workgroup owns 8 hidden outputs of one token;
-//   wave w streams the down rows of routes j = w, w+4, ... and folds the
-//   routing weight into its fp32 accumulators (j ascending). Lanes of a wave
-//   are split into slots of pow2(I/32) lanes; a slot owns rows of the 8 and
-//   its lanes cover the I/32 chunks. The four wave partials are summed in
-//   wave order and y is written once. No floating-point atomics anywhere.
+//   (token t, expert e) and streams their gate and up rows, lane l covering
+//   the 32-element chunks c = l, l+64, ... of the reduction (H); waves are
+//   independent (no workgroup barrier), so each computes as soon as its own
+//   loads land. Weights are unpacked to bf16 (128 + q) pairs and
+//   multiplied with the bf16 activation pairs by v_dot2c_f32_bf16 (exact
+//   products, fp32 sums); per chunk the bias and zero point are removed in
+//   fp32: s * (sum x(128+q) - (128+z) sum x). A DPP butterfly reduces each
+//   row; silu(gate) * up goes to the fp32 intermediate a[r][i].
+// Kernel 2 (down + combine): a workgroup owns kDownRows hidden outputs of
+//   one token; wave w streams the down rows of routes j = w, w+8, ... and
+//   folds the routing weight into its fp32 accumulators. The token's
+//   intermediate rows and the tile's scales and zeros are staged in LDS.
+//   Lanes of a wave form slots of pow2(I/32) lanes; a slot owns some of the
+//   rows and its lanes cover the I/32 chunks. The eight wave partials are
+//   added in wave (= route) order and y is written once. No floating-point
+//   atomics anywhere.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,23 +31,44 @@ namespace moe {
 namespace {
 
 constexpr int kGateUpThreads = 256;
-constexpr int kDownThreads = 256;
+constexpr int kGateUpWaves = kGateUpThreads / kWave;
+constexpr int kNpw = 2;                       // neurons per wave
+constexpr int kDownWaves = 8;
+constexpr int kDownThreads = kDownWaves * kWave;
 constexpr int kDownRows = 8;
+constexpr size_t kMaxDownLds = 48 * 1024;     // staged intermediate rows + scales + zeros
 
-template <int kNpw>
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, the same bits in every lane: butterflies
+// inside each 16-lane row with DPP (xor 1, xor 2, half-row mirror, row
+// mirror), then the four row sums added as (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
     const uint8_t* __restrict__ zp, float* __restrict__ a, int mk, int k, int E, int H,
     int I, int g) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave_id = blockIdx.x * (kGateUpThreads / kWave) + threadIdx.x / kWave;
-  const int nwaves = gridDim.x * (kGateUpThreads / kWave);
+  const int wave_id = blockIdx.x * kGateUpWaves + threadIdx.x / kWave;
+  const int nwaves = gridDim.x * kGateUpWaves;
   const int tasks_per_route = I / kNpw;
   const int ntasks = mk * tasks_per_route;
-  const int nch = H >> 5;
-  const int words = H >> 3;
-  const int gpr = H / g;
+  const int nch = H >> 5, words = H >> 3, gpr = H / g;
 
   for (int task = wave_id; task < ntasks; task += nwaves) {
     const int r = task / tasks_per_route;
@@ -57,7 +82,6 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     float acc[2 * kNpw];
 #pragma unroll
     for (int j = 0; j < 2 * kNpw; ++j) acc[j] = 0.0f;
-
     const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
     for (int c = lane; c < nch; c += kWave) {
       // Issue the weight loads first so they are all in flight together.
@@ -76,7 +100,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const uint4 t4 = xrow[c * 4 + v];
-        xw[4 * v + 0] = t4.x; xw[4 * v + 1] = t4.y; xw[4 * v + 2] = t4.z; xw[4 * v + 3] = t4.w;
+        xw[4 * v] = t4.x; xw[4 * v + 1] = t4.y; xw[4 * v + 2] = t4.z; xw[4 * v + 3] = t4.w;
       }
       float sx = 0.0f;
 #pragma unroll
@@ -96,7 +120,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
       }
     }
 #pragma unroll
-    for (int j = 0; j < 2 * kNpw; ++j) acc[j] = wave_sum(acc[j]);
+    for (int j = 0; j < 2 * kNpw; ++j) acc[j] = wave_sum_dpp(acc[j]);
     float gv = acc[0], uv = acc[kNpw];
 #pragma unroll
     for (int j = 1; j < kNpw; ++j) {
@@ -106,103 +130,137 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
   }
 }
 
+// kRps: rows per lane, ceil(kDownRows / slots); kKpw: routes per wave.
+template <int kKpw, int kRps>
 __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
     const float* __restrict__ a, const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, const uint32_t* __restrict__ q,
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zp, float* __restrict__ y,
     int M, int k, int E, int H, int I, int g) {
-  __shared__ float part[kDownThreads / kWave][kDownRows];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int nwv = kDownThreads / kWave;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int gpr = I / g;
+  float* as = reinterpret_cast<float*>(lds);                  // [k][I] intermediate rows
+  float* ss = as + static_cast<size_t>(k) * I;                // [k][kDownRows][gpr] scales
+  float* zs = ss + k * kDownRows * gpr;                       // [k][kDownRows][gpr] zeros
+  int* es = reinterpret_cast<int*>(zs + k * kDownRows * gpr);  // [k] experts
+  __shared__ float part[kDownWaves][kDownRows];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int tiles_per_tok = H / kDownRows;
   const int ntiles = M * tiles_per_tok;
-  const int nch = I >> 5;
-  const int words = I >> 3;
-  const int gpr = I / g;
-  // Lanes form slots of `span` lanes (a power of two >= the chunk count, or
-  // the whole wave when a row has more than 64 chunks).
+  const int nch = I >> 5, words = I >> 3;
   int span = 1;
   while (span < nch && span < kWave) span <<= 1;
   const int slots = kWave / span;
   const int slot = lane / span;
   const int c0 = lane - slot * span;
-  const int rps = (kDownRows + slots - 1) / slots;  // rows per slot
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t = tile / tiles_per_tok;
     const int h0 = (tile - t * tiles_per_tok) * kDownRows;
-    float acc[kDownRows];
+    int ex[kKpw];
+    float wr[kKpw];
 #pragma unroll
-    for (int i = 0; i < kDownRows; ++i) acc[i] = 0.0f;
-
-    for (int j = wave; j < k; j += nwv) {
-      const int r = t * k + j;
-      const int e = load_expert(ids, r, E);
-      if (e < 0) continue;
-      const float wj = topk_w[r];
-      for (int c = c0; c < nch; c += span) {
-        uint4 wv[kDownRows];
-        float s[kDownRows], z[kDownRows];
+    for (int u = 0; u < kKpw; ++u) {
+      const int j = wave + kDownWaves * u;
+      ex[u] = j < k ? load_expert(ids, t * k + j, E) : -1;
+      wr[u] = j < k ? topk_w[t * k + j] : 0.0f;
+    }
+    // Weight loads of this wave's routes (two chunks per lane at most).
+    constexpr int kMaxCh = 2;
+    uint4 wv[kKpw][kMaxCh][kRps];
 #pragma unroll
-        for (int i = 0; i < kDownRows; ++i) {
+    for (int u = 0; u < kKpw; ++u) {
+      if (ex[u] < 0) continue;
+#pragma unroll
+      for (int cc = 0; cc < kMaxCh; ++cc) {
+        const int c = c0 + cc * span;
+        if (c >= nch) continue;
+#pragma unroll
+        for (int i = 0; i < kRps; ++i) {
           const int m = slot + i * slots;
-          if (i < rps && m < kDownRows) {
-            const size_t row = static_cast<size_t>(e) * H + h0 + m;
-            const int grp = (c << 5) / g;
-            wv[i] = load_stream16(q + row * words + 4 * c);
-            s[i] = half_bits_to_float(sc[row * gpr + grp]);
-            z[i] = static_cast<float>(zp[row * gpr + grp]);
+          if (m < kDownRows) {
+            const size_t row = static_cast<size_t>(ex[u]) * H + h0 + m;
+            wv[u][cc][i] = load_stream16(q + row * words + 4 * c);
           }
         }
-        const float4* ap = reinterpret_cast<const float4*>(a + static_cast<size_t>(r) * I + (c << 5));
-        float av[32];
+      }
+    }
+    // Stage the token's intermediate rows, and the tile's scales and zeros.
+    const float4* ag = reinterpret_cast<const float4*>(a + static_cast<size_t>(t) * k * I);
+    for (int v = threadIdx.x; v < k * I / 4; v += kDownThreads) reinterpret_cast<float4*>(as)[v] = ag[v];
+    if (threadIdx.x < k) es[threadIdx.x] = load_expert(ids, t * k + threadIdx.x, E);
+    __syncthreads();
+    for (int v = threadIdx.x; v < k * kDownRows * gpr; v += kDownThreads) {
+      const int j = v / (kDownRows * gpr);
+      const int rem = v - j * kDownRows * gpr;
+      const int e = es[j];
+      if (e >= 0) {
+        const size_t off = (static_cast<size_t>(e) * H + h0) * gpr + rem;
+        ss[v] = half_bits_to_float(sc[off]);
+        zs[v] = static_cast<float>(zp[off]);
+      }
+    }
+    __syncthreads();
+
+    float acc[kRps];
+#pragma unroll
+    for (int i = 0; i < kRps; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kKpw; ++u) {
+      if (ex[u] < 0) continue;
+      const int j = wave + kDownWaves * u;
+#pragma unroll
+      for (int cc = 0; cc < kMaxCh; ++cc) {
+        const int c = c0 + cc * span;
+        if (c >= nch) continue;
+        const int grp = (c << 5) / g;
+        float af[32];
+        const float4* ap = reinterpret_cast<const float4*>(as + static_cast<size_t>(j) * I + (c << 5));
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const float4 t4 = ap[v];
-          av[4 * v] = t4.x; av[4 * v + 1] = t4.y; av[4 * v + 2] = t4.z; av[4 * v + 3] = t4.w;
+          af[4 * v] = t4.x; af[4 * v + 1] = t4.y; af[4 * v + 2] = t4.z; af[4 * v + 3] = t4.w;
         }
         float sa = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 32; ++v) sa += av[v];
+        for (int v = 0; v < 32; ++v) sa += af[v];
 #pragma unroll
-        for (int i = 0; i < kDownRows; ++i) {
+        for (int i = 0; i < kRps; ++i) {
           const int m = slot + i * slots;
-          if (i < rps && m < kDownRows) {
-            const uint32_t w4[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+          if (m < kDownRows) {
+            const int si = (j * kDownRows + m) * gpr + grp;
+            const uint32_t w4[4] = {wv[u][cc][i].x, wv[u][cc][i].y, wv[u][cc][i].z, wv[u][cc][i].w};
             float d = 0.0f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               float qf[8];
               unpack8_f32(w4[v], qf);
 #pragma unroll
-              for (int u = 0; u < 8; ++u) d = fmaf(av[8 * v + u], qf[u], d);
+              for (int e8 = 0; e8 < 8; ++e8) d = fmaf(af[8 * v + e8], qf[e8], d);
             }
-            acc[i] = fmaf(wj * s[i], fmaf(-z[i], sa, d), acc[i]);
+            acc[i] = fmaf(wr[u] * ss[si], fmaf(-zs[si], sa, d), acc[i]);
           }
         }
       }
     }
     // Sum each row over the lanes of its slot (butterfly inside the span).
 #pragma unroll
-    for (int i = 0; i < kDownRows; ++i) {
-      if (i < rps) {
-        float v = acc[i];
-        for (int o = span >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-        acc[i] = v;
-      }
+    for (int i = 0; i < kRps; ++i) {
+      float v = acc[i];
+      for (int o = span >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+      acc[i] = v;
     }
     if (c0 == 0) {
 #pragma unroll
-      for (int i = 0; i < kDownRows; ++i) {
+      for (int i = 0; i < kRps; ++i) {
         const int m = slot + i * slots;
-        if (i < rps && m < kDownRows) part[wave][m] = acc[i];
+        if (m < kDownRows) part[wave][m] = acc[i];
       }
     }
     __syncthreads();
     if (threadIdx.x < kDownRows) {
       float v = part[0][threadIdx.x];
-      for (int w = 1; w < nwv; ++w) v += part[w][threadIdx.x];
+      for (int w = 1; w < kDownWaves; ++w) v += part[w][threadIdx.x];
       y[static_cast<size_t>(t) * H + h0 + threadIdx.x] = v;
     }
     __syncthreads();
@@ -214,32 +272,55 @@ int grid_for(int work_groups, int max_workgroups) {
   return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : work_groups;
 }
 
+size_t down_lds(int I, int k, int g) {
+  return sizeof(float) * (static_cast<size_t>(k) * I + 2 * static_cast<size_t>(k) * kDownRows * (I / g)) +
+         sizeof(int) * static_cast<size_t>(k);
+}
+
+template <int kKpw, int kRps>
+void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_down_int4<kKpw, kRps>), dim3(wgs), dim3(kDownThreads),
+                     down_lds(p.I, p.k, p.w2.group), stream, p.a, p.ids, p.topk_w,
+                     static_cast<const uint32_t*>(p.w2.q), static_cast<const uint16_t*>(p.w2.scale),
+                     p.w2.zero, p.y, p.M, p.k, p.E, p.H, p.I, p.w2.group);
+}
+
+template <int kKpw>
+void launch_down_rps(const DecodeArgs& p, int wgs, hipStream_t stream) {
+  int nch = p.I >> 5, span = 1;
+  while (span < nch && span < kWave) span <<= 1;
+  const int slots = kWave / span;
+  const int rps = (kDownRows + slots - 1) / slots;
+  if (rps <= 1) launch_down<kKpw, 1>(p, wgs, stream);
+  else if (rps <= 2) launch_down<kKpw, 2>(p, wgs, stream);
+  else if (rps <= 4) launch_down<kKpw, 4>(p, wgs, stream);
+  else launch_down<kKpw, 8>(p, wgs, stream);
+}
+
 }  // namespace
 
-constexpr int kDecodeNpw = 2;
-
-bool decode_shape_ok(int H, int I, int k) {
-  return (H % 32) == 0 && (I % 32) == 0 && (I % kDecodeNpw) == 0 && (H % kDownRows) == 0 && k >= 1;
+bool decode_shape_ok(int H, int I, int k, int g13, int g2) {
+  // Two 32-element chunks of a down row per lane at most (I <= 4096), and the
+  // staged intermediate rows of one token fit in LDS.
+  (void)g13;
+  return (H % 32) == 0 && (I % 32) == 0 && I <= 4096 && (I % kNpw) == 0 &&
+         (H % kDownRows) == 0 && k >= 1 && k <= 2 * kDownWaves && down_lds(I, k, g2) <= kMaxDownLds;
 }
 
 hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const int mk = p.M * p.k;
-  const int waves = mk * (p.I / kDecodeNpw);
-  const int wgs = grid_for((waves + 3) / 4, p.max_workgroups);
-  hipLaunchKernelGGL(decode_gate_up_int4<kDecodeNpw>, dim3(wgs), dim3(kGateUpThreads), 0, stream,
-                     p.x, p.ids, static_cast<const uint32_t*>(p.w13.q),
-                     static_cast<const uint16_t*>(p.w13.scale), p.w13.zero, p.a, mk, p.k, p.E,
-                     p.H, p.I, p.w13.group);
+  const int waves = mk * (p.I / kNpw);
+  const int wgs = grid_for((waves + kGateUpWaves - 1) / kGateUpWaves, p.max_workgroups);
+  hipLaunchKernelGGL(decode_gate_up_int4, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids,
+                     static_cast<const uint32_t*>(p.w13.q), static_cast<const uint16_t*>(p.w13.scale),
+                     p.w13.zero, p.a, mk, p.k, p.E, p.H, p.I, p.w13.group);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream) {
-  const int tiles = p.M * (p.H / kDownRows);
-  const int wgs = grid_for(tiles, p.max_workgroups);
-  hipLaunchKernelGGL(decode_down_int4, dim3(wgs), dim3(kDownThreads), 0, stream, p.a, p.ids,
-                     p.topk_w, static_cast<const uint32_t*>(p.w2.q),
-                     static_cast<const uint16_t*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E,
-                     p.H, p.I, p.w2.group);
+  const int wgs = grid_for(p.M * (p.H / kDownRows), p.max_workgroups);
+  if (p.k <= kDownWaves) launch_down_rps<1>(p, wgs, stream);
+  else launch_down_rps<2>(p, wgs, stream);
   return hipGetLastError();
 }
 

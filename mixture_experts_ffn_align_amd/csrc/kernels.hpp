@@ -25,7 +25,7 @@ struct DecodeArgs {
   int M, H, I, E, k;
   int max_workgroups;
 };
-bool decode_shape_ok(int H, int I, int k);
+bool decode_shape_ok(int H, int I, int k, int g13, int g2);
 hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream);
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream);
 
