@@ -5,31 +5,34 @@
 // Section 3.4: grouped GEMM over routing-dependent token counts, weights as
 // the left operand so Y_e^T = W_e X_e^T).
 //
-// Both GEMMs put the expert's weight rows on the MFMA A operand and the
-// block's tokens (16 per sub-tile) on B, with v_mfma_f32_16x16x32_bf16:
+// A workgroup takes one aligned block (b <= 64 routes of one expert, four
+// 16-token sub-tiles) and 64 output rows; wave w owns rows 16w..16w+15.
+// Every GEMM uses v_mfma_f32_16x16x32_bf16 with the expert's weight rows on
+// the A operand and the block's tokens on B:
 //   A lane l: weight row l%16, 8 reduction elements of lane group l/16;
 //   B lane l: token column l%16, the same 8 reduction elements;
 //   D lane l: rows 4*(l/16)+i (i < 4) of column l%16.
-// A slab of 32*kSpw reduction elements lies inside one quantisation group;
-// lane group q holds words kSpw*q .. kSpw*q+kSpw-1 of the slab (one 4*kSpw-byte
-// load per lane and row), and MFMA step j of the slab uses word kSpw*q + j.
-// Weights are dequantised exactly to bf16 (q - z is an integer in [-15, 15]),
-// and each slab's fp32 partial is multiplied by the group scale before it is
-// added to the accumulator, so the only rounding is fp32 accumulation.
+// The reduction runs in slabs of 32*kSpw elements, each inside one
+// quantisation group; lane group q holds words kSpw*q .. kSpw*q+kSpw-1 of a
+// slab row and MFMA step j uses word kSpw*q + j. The block's activations for
+// a slab are staged in LDS (double-buffered: the next slab's global loads
+// are in flight while the current slab's MFMAs run) and shared by the four
+// waves; each wave streams only its own weight rows, one slab ahead, straight
+// into registers. Sub-tiles with no valid route are skipped.
 //
-// gate/up: one workgroup per (aligned block, 16 neurons); the four waves
-//   split the reduction (H) into quarters and their partials are summed in
-//   wave order through LDS. Each wave prefetches its next slab's weights and
-//   activations while the current slab's MFMAs run. The epilogue writes
-//   silu(gate)*up for every valid route of the block as a bf16 hi/lo pair
-//   (a = hi + lo to within 2^-17 relative), ready to be the B operand of the
-//   down GEMM.
-// down: one workgroup per (aligned block, 16 hidden rows), the same K split;
-//   B = the hi and lo planes of the intermediate (two MFMAs per step). Each
-//   route's yhat row is written once.
+// gate/up: the int4 words become bf16 (128 + q) pairs with one AND-OR (AWQ
+//   nibble order) and a second MFMA per step adds -(128 + z) times the same
+//   activations, so each slab's accumulator holds sum x (q - z) for the
+//   group; it is scaled by the group scale in fp32. The epilogue writes
+//   silu(gate) * up for every valid route as a bf16 hi/lo pair (a = hi + lo
+//   to within 2^-17 relative), the B operand of the down GEMM.
+// down: the weights are dequantised exactly to bf16 integers (q - z lies in
+//   [-15, 15]) and two MFMAs per step take the hi and lo planes of the
+//   intermediate. Each route's yhat row is written once.
 // combine: y[t] = sum over j ascending of w[t,j] * yhat[t*k+j].
 // Workgroups whose block lies past num_padded (read on the device) exit at
-// once, so the grid can be sized from the host-known capacity.
+// once, so the grid can be sized from the host-known capacity. No
+// floating-point atomics; every sum has a fixed order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,10 +41,27 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxSub = 4;        // 16-token sub-tiles per block (b <= 64)
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTileRows = 16 * kWaves;   // output rows per workgroup
+constexpr int kMaxTok = 64;              // block size limit: four 16-token sub-tiles
+constexpr int kMaxSub = kMaxTok / 16;
 
 __device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One packed word -> eight bf16 (128 + q), element order.
+__device__ __forceinline__ bf16x8 bias_pairs(uint32_t w) {
+  uint32_t p[4];
+  unpack8_bias128(w, p);
+  return __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+}
+
+// Eight copies of the bf16 value -(128 + z), z in 0..15.
+__device__ __forceinline__ bf16x8 neg_zero_pairs(uint32_t z) {
+  const uint32_t h = 0xC300u | z;
+  const uint32_t pr = h | (h << 16);
+  return __builtin_bit_cast(bf16x8, make_uint4(pr, pr, pr, pr));
 }
 
 // One packed word -> eight exact bf16 values (q - z), element order.
@@ -54,57 +74,57 @@ __device__ __forceinline__ bf16x8 dequant8_exact(uint32_t w, float z) {
   return r;
 }
 
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+template <int kSpw>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[kSpw]) {
+  if constexpr (kSpw == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (kSpw == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = p[0];
+  }
 }
 
-// Columns of one aligned block: route IDs (or -1) for the four sub-tiles of
-// lane column n, and which sub-tiles hold at least one valid route.
-struct BlockCols {
+// Route of every column of the block (-1 for padding), staged in LDS, and
+// the per-lane view: route of column n of each sub-tile and which sub-tiles
+// hold a valid route.
+struct BlockView {
   int rid[kMaxSub];
-  bool any[kMaxSub];
+  bool act[kMaxSub];
 };
 
-__device__ __forceinline__ BlockCols load_block_cols(const int32_t* sorted, int blk, int b, int nst,
-                                                     int mk, int n) {
-  BlockCols bc;
-#pragma unroll
-  for (int st = 0; st < kMaxSub; ++st) {
-    const int col = 16 * st + n;
+__device__ __forceinline__ BlockView stage_block(const int32_t* sorted, int blk, int b, int mk,
+                                                 int* cols, int n) {
+  if (threadIdx.x < kMaxTok) {
     int r = -1;
-    if (st < nst && col < b) {
-      r = sorted[static_cast<size_t>(blk) * b + col];
+    if (static_cast<int>(threadIdx.x) < b) {
+      r = sorted[static_cast<size_t>(blk) * b + threadIdx.x];
       if (r < 0 || r >= mk) r = -1;
     }
-    bc.rid[st] = r;
-    bc.any[st] = __ballot(r >= 0) != 0ull;
-  }
-  return bc;
-}
-
-// Reduction across the four waves of a workgroup, in wave order, through
-// LDS. `part` holds kWaves x nvals x 64 floats.
-template <int kVals>
-__device__ __forceinline__ void reduce_waves(float (&v)[kVals], float* part, int wave, int lane) {
-  constexpr int kWaves = kThreads / kWave;
-#pragma unroll
-  for (int i = 0; i < kVals; ++i) part[(wave * kVals + i) * kWave + lane] = v[i];
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int i = 0; i < kVals; ++i) {
-      float s = part[i * kWave + lane];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) s += part[(w * kVals + i) * kWave + lane];
-      v[i] = s;
-    }
+    cols[threadIdx.x] = r;
   }
   __syncthreads();
+  BlockView v;
+#pragma unroll
+  for (int st = 0; st < kMaxSub; ++st) {
+    v.rid[st] = cols[16 * st + n];
+    v.act[st] = __ballot(v.rid[st] >= 0) != 0ull;
+  }
+  return v;
 }
 
-// gate/up: workgroup = (aligned block, 16 neurons); wave w reduces over the
-// w-th quarter of H. Per slab, the wave dequantises its gate and up words
-// once and runs them against every active 16-token sub-tile.
+// Weight words of a wave run kDepth slabs ahead of the MFMAs in a register
+// ring (the ring index is static: the slab loop is unrolled by kDepth), so
+// each wave keeps kDepth slabs of its weight rows in flight; kDepth * kSpw
+// words (256 reduction elements) per lane and row.
+#ifndef MOE_RING_WORDS
+#define MOE_RING_WORDS 4
+#endif
+template <int kSpw>
+constexpr int ring_depth() { return MOE_RING_WORDS / kSpw > 0 ? MOE_RING_WORDS / kSpw : 1; }
+
 template <int kSpw>
 __global__ __launch_bounds__(kThreads) void grouped_gate_up_int4(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted,
@@ -112,131 +132,157 @@ __global__ __launch_bounds__(kThreads) void grouped_gate_up_int4(
     const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
     const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
     int mk, int k, int E, int H, int I, int g, int b, int nblk) {
-  constexpr int kWaves = kThreads / kWave;
   constexpr int kSlab = 32 * kSpw;
-  constexpr int kVals = kMaxSub * 8;  // gate and up, 4 rows each, per sub-tile
-  __shared__ float part[kWaves * kVals * kWave];
+  constexpr int kRowB = kSlab * 2 + 16;          // bytes per staged token row (padded)
+  constexpr int kChunks = kSlab / 8;             // 16-byte chunks per token row
+  constexpr int kMaxGroups = 64;                 // H / g held in LDS (H <= 8192 at g = 128)
+  constexpr int kDepth = ring_depth<kSpw>();
+  __shared__ __align__(16) unsigned char bs[2][kMaxTok * kRowB];
+  __shared__ uint16_t ssh[2 * kTileRows * kMaxGroups / 4];   // this tile's scales: [2*64 rows][gpr]
+  __shared__ uint8_t szz[2 * kTileRows * kMaxGroups / 4];    // and zeros
+  __shared__ int cols[kMaxTok];
+  __shared__ int toks[kMaxTok];                              // token of each block column, -1 if none
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, lq = lane >> 4;
-  const int ntiles = I / 16;
-  const int ntasks = nblk * ntiles;
+  const int ngroups = I / kTileRows;
+  const int ntasks = nblk * ngroups;
   const int npad = num_padded[0];
-  const int nst = (b + 15) / 16;
   const int words = H >> 3, gpr = H / g;
-  const int kq = H / kWaves;                 // reduction range of one wave
-  const int nslab = kq / kSlab;
+  const int nslab = H / kSlab;
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-    const int blk = task / ntiles;
-    const int nt = (task - blk * ntiles) * 16;
+    const int blk = task / ngroups;
+    const int ng = task - blk * ngroups;
     if (blk * b >= npad) continue;
     const int e = blocks[blk];
     if (e < 0 || e >= E) continue;
-    const BlockCols bc = load_block_cols(sorted, blk, b, nst, mk, n);
-    int tok[kMaxSub];
-#pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) tok[st] = bc.rid[st] >= 0 ? bc.rid[st] / k : 0;
 
-    const size_t rowg = static_cast<size_t>(e) * (2 * I) + nt;  // first gate row of the tile
-    const size_t rowu = rowg + I;                                 // first up row
-    const int kbeg = wave * kq;
-    const uint32_t* qg = q + (rowg + n) * words + (kbeg >> 3) + kSpw * lq;
-    const uint32_t* qu = q + (rowu + n) * words + (kbeg >> 3) + kSpw * lq;
+    // Weight rows of this wave: gate rows and up rows of 16 neurons.
+    const size_t tile0 = static_cast<size_t>(e) * (2 * I) + ng * kTileRows;
+    const size_t rowg = tile0 + wave * 16;
+    const size_t rowu = rowg + I;
+    const uint32_t* qg = q + (rowg + n) * words + kSpw * lq;
+    const uint32_t* qu = q + (rowu + n) * words + kSpw * lq;
+    uint32_t wg[kDepth][kSpw], wu[kDepth][kSpw];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      if (d < nslab) {
+        load_words<kSpw>(qg + d * 4 * kSpw, wg[d]);
+        load_words<kSpw>(qu + d * 4 * kSpw, wu[d]);
+      }
+    }
+    // Scales and zeros of the tile's 64 gate and 64 up rows, for all groups.
+    for (int v = threadIdx.x; v < 2 * kTileRows * gpr; v += kThreads) {
+      const int half = v / (kTileRows * gpr);
+      const size_t off = (tile0 + half * static_cast<size_t>(I)) * gpr + (v - half * kTileRows * gpr);
+      ssh[v] = sc[off];
+      szz[v] = zp[off];
+    }
+    if (threadIdx.x < kMaxTok) {
+      const int c = threadIdx.x;
+      int r = c < b ? sorted[static_cast<size_t>(blk) * b + c] : -1;
+      toks[c] = (r >= 0 && r < mk) ? r / k : -1;
+    }
+    const BlockView bv = stage_block(sorted, blk, b, mk, cols, n);   // includes a barrier
+
+    uint4 breg[kSpw];
+    auto load_b = [&](int s) {
+#pragma unroll
+      for (int u = 0; u < kSpw; ++u) {
+        const int idx = threadIdx.x + kThreads * u;
+        const int col = idx / kChunks, ch = idx - col * kChunks;
+        const int t = toks[col];
+        breg[u] = t >= 0 ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + s * kSlab + ch * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_b = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < kSpw; ++u) {
+        const int idx = threadIdx.x + kThreads * u;
+        const int col = idx / kChunks, ch = idx - col * kChunks;
+        *reinterpret_cast<uint4*>(&bs[buf][col * kRowB + ch * 16]) = breg[u];
+      }
+    };
 
     floatx4 accg[kMaxSub], accu[kMaxSub];
 #pragma unroll
     for (int st = 0; st < kMaxSub; ++st) { accg[st] = floatx4{0, 0, 0, 0}; accu[st] = floatx4{0, 0, 0, 0}; }
 
-    // Prefetch: the first slab's weights and activations.
-    uint32_t wg[kSpw], wu[kSpw];
-    bf16x8 Bn[kMaxSub][kSpw];
+    load_b(0);
+    store_b(0);
+    __syncthreads();
+    const int lg = wave * 16 + n;               // local row of this lane's A operand
+    for (int s0 = 0; s0 < nslab; s0 += kDepth) {
 #pragma unroll
-    for (int j = 0; j < kSpw; ++j) { wg[j] = qg[j]; wu[j] = qu[j]; }
+      for (int d = 0; d < kDepth; ++d) {
+        const int s = s0 + d;
+        if (s >= nslab) break;
+        const int cur = s & 1;
+        const int grp = (s * kSlab) / g;
+        bf16x8 Ag[kSpw], Au[kSpw];
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) {
-      if (!bc.any[st]) continue;
-      const uint16_t* xp = x + static_cast<size_t>(tok[st]) * H + kbeg + 8 * kSpw * lq;
-#pragma unroll
-      for (int j = 0; j < kSpw; ++j) Bn[st][j] = load_bf16x8(xp + 8 * j);
-    }
-    for (int sl = 0; sl < nslab; ++sl) {
-      const int k0 = kbeg + sl * kSlab;
-      const int grp = k0 / g;
-      const float zg = static_cast<float>(zp[(rowg + n) * gpr + grp]);
-      const float zu = static_cast<float>(zp[(rowu + n) * gpr + grp]);
-      float sg[4], su[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sg[i] = half_bits_to_float(sc[(rowg + 4 * lq + i) * gpr + grp]);
-        su[i] = half_bits_to_float(sc[(rowu + 4 * lq + i) * gpr + grp]);
-      }
-      bf16x8 Ag[kSpw], Au[kSpw], B[kMaxSub][kSpw];
-#pragma unroll
-      for (int j = 0; j < kSpw; ++j) { Ag[j] = dequant8_exact(wg[j], zg); Au[j] = dequant8_exact(wu[j], zu); }
-#pragma unroll
-      for (int st = 0; st < kMaxSub; ++st)
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) B[st][j] = Bn[st][j];
-      if (sl + 1 < nslab) {   // next slab's loads overlap this slab's MFMAs
-        const int w1 = (sl + 1) * kSpw * 4;
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) { wg[j] = qg[w1 + j]; wu[j] = qu[w1 + j]; }
-#pragma unroll
-        for (int st = 0; st < kMaxSub; ++st) {
-          if (!bc.any[st]) continue;
-          const uint16_t* xp = x + static_cast<size_t>(tok[st]) * H + k0 + kSlab + 8 * kSpw * lq;
-#pragma unroll
-          for (int j = 0; j < kSpw; ++j) Bn[st][j] = load_bf16x8(xp + 8 * j);
+        for (int j = 0; j < kSpw; ++j) { Ag[j] = bias_pairs(wg[d][j]); Au[j] = bias_pairs(wu[d][j]); }
+        // Activation loads before the weight-ring loads: the wait before
+        // store_b then leaves the (later) weight loads in flight.
+        if (s + 1 < nslab) load_b(s + 1);
+        if (s + kDepth < nslab) {
+          load_words<kSpw>(qg + (s + kDepth) * 4 * kSpw, wg[d]);
+          load_words<kSpw>(qu + (s + kDepth) * 4 * kSpw, wu[d]);
         }
-      }
-#pragma unroll
-      for (int st = 0; st < kMaxSub; ++st) {
-        if (!bc.any[st]) continue;
-        floatx4 dg = {0, 0, 0, 0}, du = {0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) {
-          dg = mfma_bf16(Ag[j], B[st][j], dg);
-          du = mfma_bf16(Au[j], B[st][j], du);
-        }
+        const bf16x8 Zg = neg_zero_pairs(szz[lg * gpr + grp]);
+        const bf16x8 Zu = neg_zero_pairs(szz[(kTileRows + lg) * gpr + grp]);
+        float cg[4], cu[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          accg[st][i] = fmaf(sg[i], dg[i], accg[st][i]);
-          accu[st][i] = fmaf(su[i], du[i], accu[st][i]);
+          cg[i] = half_bits_to_float(ssh[(wave * 16 + 4 * lq + i) * gpr + grp]);
+          cu[i] = half_bits_to_float(ssh[(kTileRows + wave * 16 + 4 * lq + i) * gpr + grp]);
         }
+#pragma unroll
+        for (int st = 0; st < kMaxSub; ++st) {
+          if (!bv.act[st]) continue;
+          const unsigned char* brow = &bs[cur][(16 * st + n) * kRowB + 16 * kSpw * lq];
+          floatx4 dg = {0, 0, 0, 0}, du = {0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < kSpw; ++j) {
+            const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(brow + 16 * j));
+            dg = mfma_bf16(Ag[j], B, dg);
+            dg = mfma_bf16(Zg, B, dg);
+            du = mfma_bf16(Au[j], B, du);
+            du = mfma_bf16(Zu, B, du);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            accg[st][i] = fmaf(cg[i], dg[i], accg[st][i]);
+            accu[st][i] = fmaf(cu[i], du[i], accu[st][i]);
+          }
+        }
+        if (s + 1 < nslab) store_b(cur ^ 1);
+        __syncthreads();
       }
     }
-    float v[kVals];
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st)
+    for (int st = 0; st < kMaxSub; ++st) {
+      const int r = bv.rid[st];
+      if (r < 0) continue;
+      uint32_t hi2[2], lo2[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { v[st * 8 + i] = accg[st][i]; v[st * 8 + 4 + i] = accu[st][i]; }
-    reduce_waves(v, part, wave, lane);
-    if (wave == 0) {
-#pragma unroll
-      for (int st = 0; st < kMaxSub; ++st) {
-        const int r = bc.rid[st];
-        if (r < 0) continue;
-        uint32_t hi2[2], lo2[2];
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float v0 = silu_mul(v[st * 8 + i], v[st * 8 + 4 + i]);
-          const float v1 = silu_mul(v[st * 8 + i + 1], v[st * 8 + 4 + i + 1]);
-          const bf16x2 h = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
-          const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-          const bf16x2 l = {static_cast<__bf16>(v0 - bf16_lo(hb)), static_cast<__bf16>(v1 - bf16_hi(hb))};
-          hi2[i / 2] = hb;
-          lo2[i / 2] = __builtin_bit_cast(uint32_t, l);
-        }
-        const size_t off = static_cast<size_t>(r) * I + nt + 4 * lq;
-        *reinterpret_cast<uint2*>(a_hi + off) = make_uint2(hi2[0], hi2[1]);
-        *reinterpret_cast<uint2*>(a_lo + off) = make_uint2(lo2[0], lo2[1]);
+      for (int i = 0; i < 4; i += 2) {
+        const float v0 = silu_mul(accg[st][i], accu[st][i]);
+        const float v1 = silu_mul(accg[st][i + 1], accu[st][i + 1]);
+        const bf16x2 h = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const bf16x2 l = {static_cast<__bf16>(v0 - bf16_lo(hb)), static_cast<__bf16>(v1 - bf16_hi(hb))};
+        hi2[i / 2] = hb;
+        lo2[i / 2] = __builtin_bit_cast(uint32_t, l);
       }
+      const size_t off = static_cast<size_t>(r) * I + ng * kTileRows + wave * 16 + 4 * lq;
+      *reinterpret_cast<uint2*>(a_hi + off) = make_uint2(hi2[0], hi2[1]);
+      *reinterpret_cast<uint2*>(a_lo + off) = make_uint2(lo2[0], lo2[1]);
     }
   }
 }
 
-// down: workgroup = (aligned block, 16 hidden rows); wave w reduces over the
-// w-th quarter of I; B is the hi and lo planes of the intermediate.
 template <int kSpw>
 __global__ __launch_bounds__(kThreads) void grouped_down_int4(
     const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
@@ -244,108 +290,114 @@ __global__ __launch_bounds__(kThreads) void grouped_down_int4(
     const int32_t* __restrict__ num_padded, const uint32_t* __restrict__ q,
     const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zp, float* __restrict__ yhat,
     int mk, int E, int H, int I, int g, int b, int nblk) {
-  constexpr int kWaves = kThreads / kWave;
   constexpr int kSlab = 32 * kSpw;
-  constexpr int kVals = kMaxSub * 4;
-  __shared__ float part[kWaves * kVals * kWave];
+  constexpr int kRowB = kSlab * 2 + 16;
+  constexpr int kChunks = kSlab / 8;
+  constexpr int kLoads = 2 * kSpw;               // hi and lo planes
+  constexpr int kMaxGroups = 64;
+  constexpr int kDepth = ring_depth<kSpw>();
+  __shared__ __align__(16) unsigned char bs[2][2][kMaxTok * kRowB];
+  __shared__ uint16_t ssh[kTileRows * kMaxGroups / 2];
+  __shared__ uint8_t szz[kTileRows * kMaxGroups / 2];
+  __shared__ int cols[kMaxTok];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, lq = lane >> 4;
-  const int ntiles = H / 16;
-  const int ntasks = nblk * ntiles;
+  const int ngroups = H / kTileRows;
+  const int ntasks = nblk * ngroups;
   const int npad = num_padded[0];
-  const int nst = (b + 15) / 16;
   const int words = I >> 3, gpr = I / g;
-  const int kq = I / kWaves;
-  const int nslab = kq / kSlab;
+  const int nslab = I / kSlab;
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-    const int blk = task / ntiles;
-    const int h0 = (task - blk * ntiles) * 16;
+    const int blk = task / ngroups;
+    const int ng = task - blk * ngroups;
     if (blk * b >= npad) continue;
     const int e = blocks[blk];
     if (e < 0 || e >= E) continue;
-    const BlockCols bc = load_block_cols(sorted, blk, b, nst, mk, n);
-    int src[kMaxSub];
-#pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) src[st] = bc.rid[st] >= 0 ? bc.rid[st] : 0;
 
-    const size_t row0 = static_cast<size_t>(e) * H + h0;
-    const int kbeg = wave * kq;
-    const uint32_t* qa = q + (row0 + n) * words + (kbeg >> 3) + kSpw * lq;
+    const size_t tile0 = static_cast<size_t>(e) * H + ng * kTileRows;
+    const size_t row0 = tile0 + wave * 16;
+    const uint32_t* qa = q + (row0 + n) * words + kSpw * lq;
+    uint32_t wa[kDepth][kSpw];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (d < nslab) load_words<kSpw>(qa + d * 4 * kSpw, wa[d]);
+    for (int v = threadIdx.x; v < kTileRows * gpr; v += kThreads) {
+      ssh[v] = sc[tile0 * gpr + v];
+      szz[v] = zp[tile0 * gpr + v];
+    }
+    const BlockView bv = stage_block(sorted, blk, b, mk, cols, n);   // includes a barrier
+
+    uint4 breg[kLoads];
+    auto load_b = [&](int s) {
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int idx = threadIdx.x + kThreads * (u >> 1);
+        const int col = idx / kChunks, ch = idx - col * kChunks;
+        const int r = cols[col];
+        const uint16_t* src = (u & 1) ? a_lo : a_hi;
+        breg[u] = r >= 0 ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * I + s * kSlab + ch * 8)
+                         : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store_b = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) {
+        const int idx = threadIdx.x + kThreads * (u >> 1);
+        const int col = idx / kChunks, ch = idx - col * kChunks;
+        *reinterpret_cast<uint4*>(&bs[buf][u & 1][col * kRowB + ch * 16]) = breg[u];
+      }
+    };
+
     floatx4 acc[kMaxSub];
 #pragma unroll
     for (int st = 0; st < kMaxSub; ++st) acc[st] = floatx4{0, 0, 0, 0};
 
-    uint32_t wa[kSpw];
-    bf16x8 Hn[kMaxSub][kSpw], Ln[kMaxSub][kSpw];
+    load_b(0);
+    store_b(0);
+    __syncthreads();
+    const int la = wave * 16 + n;
+    for (int s0 = 0; s0 < nslab; s0 += kDepth) {
 #pragma unroll
-    for (int j = 0; j < kSpw; ++j) wa[j] = qa[j];
+      for (int d = 0; d < kDepth; ++d) {
+        const int s = s0 + d;
+        if (s >= nslab) break;
+        const int cur = s & 1;
+        const int grp = (s * kSlab) / g;
+        const float za = static_cast<float>(szz[la * gpr + grp]);
+        bf16x8 A[kSpw];
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) {
-      if (!bc.any[st]) continue;
-      const size_t boff = static_cast<size_t>(src[st]) * I + kbeg + 8 * kSpw * lq;
+        for (int j = 0; j < kSpw; ++j) A[j] = dequant8_exact(wa[d][j], za);
+        if (s + 1 < nslab) load_b(s + 1);
+        if (s + kDepth < nslab) load_words<kSpw>(qa + (s + kDepth) * 4 * kSpw, wa[d]);
+        float cs[4];
 #pragma unroll
-      for (int j = 0; j < kSpw; ++j) {
-        Hn[st][j] = load_bf16x8(a_hi + boff + 8 * j);
-        Ln[st][j] = load_bf16x8(a_lo + boff + 8 * j);
-      }
-    }
-    for (int sl = 0; sl < nslab; ++sl) {
-      const int k0 = kbeg + sl * kSlab;
-      const int grp = k0 / g;
-      const float za = static_cast<float>(zp[(row0 + n) * gpr + grp]);
-      float sa[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = half_bits_to_float(sc[(row0 + 4 * lq + i) * gpr + grp]);
-      bf16x8 A[kSpw], Bh[kMaxSub][kSpw], Bl[kMaxSub][kSpw];
-#pragma unroll
-      for (int j = 0; j < kSpw; ++j) A[j] = dequant8_exact(wa[j], za);
-#pragma unroll
-      for (int st = 0; st < kMaxSub; ++st)
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) { Bh[st][j] = Hn[st][j]; Bl[st][j] = Ln[st][j]; }
-      if (sl + 1 < nslab) {
-        const int w1 = (sl + 1) * kSpw * 4;
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) wa[j] = qa[w1 + j];
+        for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(ssh[(wave * 16 + 4 * lq + i) * gpr + grp]);
 #pragma unroll
         for (int st = 0; st < kMaxSub; ++st) {
-          if (!bc.any[st]) continue;
-          const size_t boff = static_cast<size_t>(src[st]) * I + k0 + kSlab + 8 * kSpw * lq;
+          if (!bv.act[st]) continue;
+          const int boff = (16 * st + n) * kRowB + 16 * kSpw * lq;
+          floatx4 dd = {0, 0, 0, 0};
 #pragma unroll
           for (int j = 0; j < kSpw; ++j) {
-            Hn[st][j] = load_bf16x8(a_hi + boff + 8 * j);
-            Ln[st][j] = load_bf16x8(a_lo + boff + 8 * j);
+            const bf16x8 Bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bs[cur][0][boff + 16 * j]));
+            const bf16x8 Bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bs[cur][1][boff + 16 * j]));
+            dd = mfma_bf16(A[j], Bh, dd);
+            dd = mfma_bf16(A[j], Bl, dd);
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[st][i] = fmaf(cs[i], dd[i], acc[st][i]);
         }
-      }
-#pragma unroll
-      for (int st = 0; st < kMaxSub; ++st) {
-        if (!bc.any[st]) continue;
-        floatx4 d = {0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) {
-          d = mfma_bf16(A[j], Bh[st][j], d);
-          d = mfma_bf16(A[j], Bl[st][j], d);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[st][i] = fmaf(sa[i], d[i], acc[st][i]);
+        if (s + 1 < nslab) store_b(cur ^ 1);
+        __syncthreads();
       }
     }
-    float v[kVals];
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[st * 4 + i] = acc[st][i];
-    reduce_waves(v, part, wave, lane);
-    if (wave == 0) {
-#pragma unroll
-      for (int st = 0; st < kMaxSub; ++st) {
-        const int r = bc.rid[st];
-        if (r < 0) continue;
-        *reinterpret_cast<float4*>(yhat + static_cast<size_t>(r) * H + h0 + 4 * lq) =
-            make_float4(v[st * 4], v[st * 4 + 1], v[st * 4 + 2], v[st * 4 + 3]);
-      }
+    for (int st = 0; st < kMaxSub; ++st) {
+      const int r = bv.rid[st];
+      if (r < 0) continue;
+      *reinterpret_cast<float4*>(yhat + static_cast<size_t>(r) * H + ng * kTileRows + wave * 16 + 4 * lq) =
+          make_float4(acc[st][0], acc[st][1], acc[st][2], acc[st][3]);
     }
   }
 }
@@ -379,32 +431,47 @@ int grid_for(int work_groups, int max_workgroups) {
   return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : work_groups;
 }
 
-int slab_words(int K, int g) {
-  // Largest of 2, 1 words per lane (slabs of 64, 32 elements) such that a
-  // slab stays inside one group and each wave's quarter of K is a whole
-  // number of slabs. (Four words per lane would double the prefetched
-  // activation registers and halve occupancy.)
-  for (int spw = 2; spw >= 1; spw >>= 1) {
+int slab_words(int K, int g, int max_spw) {
+  // Largest of 4, 2, 1 words per lane (slabs of 128, 64, 32 elements), at
+  // most max_spw, such that a slab stays inside one group and K is a whole
+  // number of slabs.
+  for (int spw = max_spw; spw >= 1; spw >>= 1) {
     const int slab = 32 * spw;
-    if (g % slab == 0 && K % (4 * slab) == 0) return spw;
+    if (g % slab == 0 && K % slab == 0) return spw;
   }
   return 0;
 }
 
+// The down kernel stages two planes, so its slab is at most 64 elements to
+// keep the double-buffered LDS tile small.
+#ifndef MOE_GATE_UP_MAX_SPW
+#define MOE_GATE_UP_MAX_SPW 4
+#endif
+constexpr int kGateUpMaxSpw = MOE_GATE_UP_MAX_SPW;
+constexpr int kDownMaxSpw = 2;
+
 }  // namespace
 
 bool grouped_shape_ok(int H, int I, int b, int g13, int g2) {
-  return b >= 1 && b <= 16 * kMaxSub && (I % 16) == 0 && (H % 16) == 0 &&
-         slab_words(H, g13) > 0 && slab_words(I, g2) > 0;
+  // The scale/zero tiles of a workgroup live in LDS: at most 16 groups per
+  // row for W13 and 32 for W2.
+  return b >= 1 && b <= kMaxTok && (I % kTileRows) == 0 && (H % kTileRows) == 0 &&
+         slab_words(H, g13, kGateUpMaxSpw) > 0 && slab_words(I, g2, kDownMaxSpw) > 0 &&
+         H / g13 <= 16 && I / g2 <= 32;
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
-  const int ntasks = p.nblk * (p.I / 16);
+  const int ntasks = p.nblk * (p.I / kTileRows);
   const int wgs = grid_for(ntasks, p.max_workgroups);
   const auto* q = static_cast<const uint32_t*>(p.w13.q);
   const auto* s = static_cast<const uint16_t*>(p.w13.scale);
   const int mk = p.M * p.k;
-  switch (slab_words(p.H, p.w13.group)) {
+  switch (slab_words(p.H, p.w13.group, kGateUpMaxSpw)) {
+    case 4:
+      hipLaunchKernelGGL(grouped_gate_up_int4<4>, dim3(wgs), dim3(kThreads), 0, stream, p.x, p.sorted,
+                         p.blocks, p.num_padded, q, s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H,
+                         p.I, p.w13.group, p.b, p.nblk);
+      break;
     case 2:
       hipLaunchKernelGGL(grouped_gate_up_int4<2>, dim3(wgs), dim3(kThreads), 0, stream, p.x, p.sorted,
                          p.blocks, p.num_padded, q, s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H,
@@ -420,12 +487,12 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
-  const int ntasks = p.nblk * (p.H / 16);
+  const int ntasks = p.nblk * (p.H / kTileRows);
   const int wgs = grid_for(ntasks, p.max_workgroups);
   const auto* q = static_cast<const uint32_t*>(p.w2.q);
   const auto* s = static_cast<const uint16_t*>(p.w2.scale);
   const int mk = p.M * p.k;
-  switch (slab_words(p.I, p.w2.group)) {
+  switch (slab_words(p.I, p.w2.group, kDownMaxSpw)) {
     case 2:
       hipLaunchKernelGGL(grouped_down_int4<2>, dim3(wgs), dim3(kThreads), 0, stream, p.a_hi, p.a_lo,
                          p.sorted, p.blocks, p.num_padded, q, s, p.w2.zero, p.yhat, mk, p.E, p.H,
