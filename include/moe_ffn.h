@@ -184,10 +184,10 @@ MOE_API int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
 MOE_API const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
 
 /* Where a forward call leaves the route-indexed intermediate silu(gate)*up
- * inside the workspace (rows of invalid routes are unspecified).
- *   format 0 (decode path): fp32 [M*k][I] at *offset (*lo_offset == *offset);
- *   format 1 (grouped path): bf16 hi plane [M*k][I] at *offset and bf16 lo plane
- *     at *lo_offset, the value being hi + lo (within 2^-17 relative). */
+ * inside the workspace (rows of invalid routes are unspecified): a bf16 hi
+ * plane [M*k][I] at *offset and a bf16 lo plane at *lo_offset, the value being
+ * hi + lo (within 2^-17 relative). *format is 1 (the only layout; 0 is
+ * reserved for an fp32 plane). */
 MOE_API moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* lo_offset,
                                 int32_t* format);
 

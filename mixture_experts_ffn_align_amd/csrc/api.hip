@@ -64,7 +64,8 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (path == MOE_PATH_DECODE) {
     if (!moe::decode_shape_ok(d->H, d->I, d->k, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
     L->off_a = 0;
-    L->total = round256(size_t(mk) * d->I * sizeof(float));
+    L->off_a_lo = round256(size_t(mk) * d->I * sizeof(uint16_t));
+    L->total = L->off_a_lo + round256(size_t(mk) * d->I * sizeof(uint16_t));
     if (L->total == 0) L->total = 256;
     return MOE_OK;
   }
@@ -112,7 +113,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
   if (L.path == MOE_PATH_DECODE) {
     moe::DecodeArgs p{};
     p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
-    p.a = at<float>(ws, L.off_a); p.y = y;
+    p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_a_lo); p.y = y;
     p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k;
     p.max_workgroups = d->max_workgroups;
     if (stages & kStageGateUp) {
@@ -308,8 +309,8 @@ moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* l
   const moe_status st = validate(d, &L, false);
   if (st != MOE_OK) return st;
   *offset = L.off_a;
-  *lo_offset = L.path == MOE_PATH_DECODE ? L.off_a : L.off_a_lo;
-  *format = L.path == MOE_PATH_DECODE ? 0 : 1;
+  *lo_offset = L.off_a_lo;
+  *format = 1;
   return MOE_OK;
 }
 

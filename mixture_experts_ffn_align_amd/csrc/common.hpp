@@ -43,6 +43,26 @@ __device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t p[4]) {
   p[3] = ((w >> 12) & m) | c;
 }
 
+// A value the compiler must keep in a VGPR. gfx9 VOP3 instructions take at
+// most one scalar or literal operand, so with the nibble mask in a VGPR and
+// the 0x43004300 constant in an SGPR each pair is a single v_and_or_b32.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// unpack8_bias128 with the nibble mask supplied in a VGPR (see in_vgpr).
+__device__ __forceinline__ void unpack8_bias128_m(uint32_t w, uint32_t m, uint32_t p[4]) {
+  const uint32_t c = 0x43004300u;
+  p[0] = (w & m) | c;
+  p[1] = ((w >> 4) & m) | c;
+  p[2] = ((w >> 8) & m) | c;
+  p[3] = ((w >> 12) & m) | c;
+}
+
+// Wave-uniform integer made explicitly scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // The eight int4 values of one word as fp32, in element order.
 __device__ __forceinline__ void unpack8_f32(uint32_t w, float q[8]) {
   const uint32_t lo = w & 0x0F0F0F0Fu;         // slots 0,2,4,6 -> elements 0,4,1,5

@@ -14,11 +14,14 @@
 //   multiplied with the bf16 activation pairs by v_dot2c_f32_bf16 (exact
 //   products, fp32 sums); per chunk the bias and zero point are removed in
 //   fp32: s * (sum x(128+q) - (128+z) sum x). A DPP butterfly reduces each
-//   row; silu(gate) * up goes to the fp32 intermediate a[r][i].
+//   row; silu(gate) * up goes to the intermediate as a bf16 hi/lo pair
+//   (a = hi + lo to within 2^-17 relative).
 // Kernel 2 (down + combine): a workgroup owns kDownRows hidden outputs of
 //   one token; wave w streams the down rows of routes j = w, w+8, ... and
 //   folds the routing weight into its fp32 accumulators. The token's
-//   intermediate rows and the tile's scales and zeros are staged in LDS.
+//   intermediate rows (hi and lo planes) and the tile's scales and zeros are
+//   staged in LDS; the weights are again bf16 (128 + q) pairs and each pair
+//   is dotted with the hi and the lo plane.
 //   Lanes of a wave form slots of pow2(I/32) lanes; a slot owns some of the
 //   rows and its lanes cover the I/32 chunks. The eight wave partials are
 //   added in wave (= route) order and y is written once. No floating-point
@@ -37,6 +40,7 @@ constexpr int kDownWaves = 8;
 constexpr int kDownThreads = kDownWaves * kWave;
 constexpr int kDownRows = 8;
 constexpr size_t kMaxDownLds = 48 * 1024;     // staged intermediate rows + scales + zeros
+constexpr int kMaxGroups = 32;                // scale groups per row held in LDS (K / g)
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
@@ -61,40 +65,64 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
-    const uint8_t* __restrict__ zp, float* __restrict__ a, int mk, int k, int E, int H,
-    int I, int g) {
+    const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
+    int mk, int k, int E, int H, int I, int g_shift) {
+  __shared__ float2 wsz[kGateUpWaves][2 * kNpw * kMaxGroups];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave_id = blockIdx.x * kGateUpWaves + threadIdx.x / kWave;
+  const int wave_l = uniform(threadIdx.x / kWave);
+  // Task indices are wave-uniform: keep them (and the row addresses) scalar.
+  const int wave_id = uniform(blockIdx.x * kGateUpWaves + threadIdx.x / kWave);
   const int nwaves = gridDim.x * kGateUpWaves;
   const int tasks_per_route = I / kNpw;
   const int ntasks = mk * tasks_per_route;
-  const int nch = H >> 5, words = H >> 3, gpr = H / g;
+  const int nch = H >> 5, words = H >> 3, gpr = H >> g_shift;
+  const uint32_t nib_mask = in_vgpr(0x000F000Fu);
 
   for (int task = wave_id; task < ntasks; task += nwaves) {
     const int r = task / tasks_per_route;
     const int i0 = (task - r * tasks_per_route) * kNpw;
-    const int e = load_expert(ids, r, E);
+    const int e = uniform(load_expert(ids, r, E));
     if (e < 0) {
-      if (lane < kNpw) a[static_cast<size_t>(r) * I + i0 + lane] = 0.0f;
+      if (lane < kNpw) {
+        a_hi[static_cast<size_t>(r) * I + i0 + lane] = 0;
+        a_lo[static_cast<size_t>(r) * I + i0 + lane] = 0;
+      }
       continue;
     }
     const int t = r / k;
+    const size_t row0 = static_cast<size_t>(e) * (2 * I) + i0;  // first gate row
+    const uint32_t* qrow[2 * kNpw];
+    const uint16_t* srow[2 * kNpw];
+    const uint8_t* zrow[2 * kNpw];
+#pragma unroll
+    for (int j = 0; j < 2 * kNpw; ++j) {
+      const size_t row = row0 + (j < kNpw ? j : I + j - kNpw);
+      qrow[j] = q + row * words;
+      srow[j] = sc + row * gpr;
+      zrow[j] = zp + row * gpr;
+    }
     float acc[2 * kNpw];
 #pragma unroll
     for (int j = 0; j < 2 * kNpw; ++j) acc[j] = 0.0f;
+    // The rows' scales and zeros: one coalesced load per lane into this
+    // wave's LDS slice (a wave reads back only what it wrote, so no barrier).
+    for (int v = lane; v < 2 * kNpw * gpr; v += kWave) {
+      const int j = v / gpr, gi = v - j * gpr;
+      wsz[wave_l][v] = make_float2(half_bits_to_float(srow[j][gi]), 128.0f + static_cast<float>(zrow[j][gi]));
+    }
     const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
     for (int c = lane; c < nch; c += kWave) {
       // Issue the weight loads first so they are all in flight together.
       uint4 wv[2 * kNpw];
       float s[2 * kNpw], zb[2 * kNpw];
-      const int grp = (c << 5) / g;
+      const int grp = (c << 5) >> g_shift;
+#pragma unroll
+      for (int j = 0; j < 2 * kNpw; ++j) wv[j] = load_stream16(qrow[j] + 4 * c);
 #pragma unroll
       for (int j = 0; j < 2 * kNpw; ++j) {
-        const int n = j < kNpw ? i0 + j : I + i0 + (j - kNpw);
-        const size_t row = static_cast<size_t>(e) * (2 * I) + n;
-        wv[j] = load_stream16(q + row * words + 4 * c);
-        s[j] = half_bits_to_float(sc[row * gpr + grp]);
-        zb[j] = 128.0f + static_cast<float>(zp[row * gpr + grp]);
+        const float2 sz = wsz[wave_l][j * gpr + grp];
+        s[j] = sz.x;
+        zb[j] = sz.y;
       }
       uint32_t xw[16];
 #pragma unroll
@@ -112,7 +140,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           uint32_t p[4];
-          unpack8_bias128(w4[v], p);
+          unpack8_bias128_m(w4[v], nib_mask, p);
 #pragma unroll
           for (int i = 0; i < 4; ++i) d = dot2_bf16(p[i], xw[4 * v + i], d);
         }
@@ -126,25 +154,33 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     for (int j = 1; j < kNpw; ++j) {
       if (lane == j) { gv = acc[j]; uv = acc[kNpw + j]; }
     }
-    if (lane < kNpw) a[static_cast<size_t>(r) * I + i0 + lane] = silu_mul(gv, uv);
+    if (lane < kNpw) {
+      const float v = silu_mul(gv, uv);
+      const __bf16 h = static_cast<__bf16>(v);
+      const size_t off = static_cast<size_t>(r) * I + i0 + lane;
+      a_hi[off] = __builtin_bit_cast(uint16_t, h);
+      a_lo[off] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v - static_cast<float>(h)));
+    }
   }
 }
 
 // kRps: rows per lane, ceil(kDownRows / slots); kKpw: routes per wave.
 template <int kKpw, int kRps>
 __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
-    const float* __restrict__ a, const int32_t* __restrict__ ids,
-    const float* __restrict__ topk_w, const uint32_t* __restrict__ q,
-    const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zp, float* __restrict__ y,
-    int M, int k, int E, int H, int I, int g) {
+    const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
+    const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
+    const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
+    const uint8_t* __restrict__ zp, float* __restrict__ y, int M, int k, int E, int H, int I,
+    int g_shift) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int gpr = I / g;
-  float* as = reinterpret_cast<float*>(lds);                  // [k][I] intermediate rows
-  float* ss = as + static_cast<size_t>(k) * I;                // [k][kDownRows][gpr] scales
-  float* zs = ss + k * kDownRows * gpr;                       // [k][kDownRows][gpr] zeros
-  int* es = reinterpret_cast<int*>(zs + k * kDownRows * gpr);  // [k] experts
+  const int gpr = I >> g_shift;
+  uint16_t* ah = reinterpret_cast<uint16_t*>(lds);                          // [k][I] hi plane
+  uint16_t* al = ah + static_cast<size_t>(k) * I;                           // [k][I] lo plane
+  float* ss = reinterpret_cast<float*>(al + static_cast<size_t>(k) * I);    // [k][kDownRows][gpr]
+  float* zs = ss + k * kDownRows * gpr;                                     // 128 + zero
   __shared__ float part[kDownWaves][kDownRows];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform(threadIdx.x / kWave);
   const int tiles_per_tok = H / kDownRows;
   const int ntiles = M * tiles_per_tok;
   const int nch = I >> 5, words = I >> 3;
@@ -153,6 +189,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
   const int slots = kWave / span;
   const int slot = lane / span;
   const int c0 = lane - slot * span;
+  const uint32_t nib_mask = in_vgpr(0x000F000Fu);
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t = tile / tiles_per_tok;
@@ -162,7 +199,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
 #pragma unroll
     for (int u = 0; u < kKpw; ++u) {
       const int j = wave + kDownWaves * u;
-      ex[u] = j < k ? load_expert(ids, t * k + j, E) : -1;
+      ex[u] = j < k ? uniform(load_expert(ids, t * k + j, E)) : -1;
       wr[u] = j < k ? topk_w[t * k + j] : 0.0f;
     }
     // Weight loads of this wave's routes (two chunks per lane at most).
@@ -171,6 +208,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
 #pragma unroll
     for (int u = 0; u < kKpw; ++u) {
       if (ex[u] < 0) continue;
+      const uint32_t* qt = q + (static_cast<size_t>(ex[u]) * H + h0) * words;
 #pragma unroll
       for (int cc = 0; cc < kMaxCh; ++cc) {
         const int c = c0 + cc * span;
@@ -178,26 +216,27 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
           const int m = slot + i * slots;
-          if (m < kDownRows) {
-            const size_t row = static_cast<size_t>(ex[u]) * H + h0 + m;
-            wv[u][cc][i] = load_stream16(q + row * words + 4 * c);
-          }
+          if (m < kDownRows) wv[u][cc][i] = load_stream16(qt + m * words + 4 * c);
         }
       }
     }
     // Stage the token's intermediate rows, and the tile's scales and zeros.
-    const float4* ag = reinterpret_cast<const float4*>(a + static_cast<size_t>(t) * k * I);
-    for (int v = threadIdx.x; v < k * I / 4; v += kDownThreads) reinterpret_cast<float4*>(as)[v] = ag[v];
-    if (threadIdx.x < k) es[threadIdx.x] = load_expert(ids, t * k + threadIdx.x, E);
-    __syncthreads();
-    for (int v = threadIdx.x; v < k * kDownRows * gpr; v += kDownThreads) {
-      const int j = v / (kDownRows * gpr);
-      const int rem = v - j * kDownRows * gpr;
-      const int e = es[j];
-      if (e >= 0) {
-        const size_t off = (static_cast<size_t>(e) * H + h0) * gpr + rem;
-        ss[v] = half_bits_to_float(sc[off]);
-        zs[v] = static_cast<float>(zp[off]);
+    const uint4* gh = reinterpret_cast<const uint4*>(a_hi + static_cast<size_t>(t) * k * I);
+    const uint4* gl = reinterpret_cast<const uint4*>(a_lo + static_cast<size_t>(t) * k * I);
+    for (int v = threadIdx.x; v < k * I / 8; v += kDownThreads) {
+      reinterpret_cast<uint4*>(ah)[v] = gh[v];
+      reinterpret_cast<uint4*>(al)[v] = gl[v];
+    }
+    // Each wave stages the scales and zeros of its own routes' rows (one
+    // coalesced load per lane); it is the only reader of that slice.
+#pragma unroll
+    for (int u = 0; u < kKpw; ++u) {
+      if (ex[u] < 0) continue;
+      const int j = wave + kDownWaves * u;
+      const size_t base = (static_cast<size_t>(ex[u]) * H + h0) * gpr;
+      for (int v = lane; v < kDownRows * gpr; v += kWave) {
+        ss[j * kDownRows * gpr + v] = half_bits_to_float(sc[base + v]);
+        zs[j * kDownRows * gpr + v] = 128.0f + static_cast<float>(zp[base + v]);
       }
     }
     __syncthreads();
@@ -213,17 +252,19 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
       for (int cc = 0; cc < kMaxCh; ++cc) {
         const int c = c0 + cc * span;
         if (c >= nch) continue;
-        const int grp = (c << 5) / g;
-        float af[32];
-        const float4* ap = reinterpret_cast<const float4*>(as + static_cast<size_t>(j) * I + (c << 5));
+        const int grp = (c << 5) >> g_shift;
+        uint32_t hw[16], lw[16];
+        const uint4* hp = reinterpret_cast<const uint4*>(ah + static_cast<size_t>(j) * I + (c << 5));
+        const uint4* lp = reinterpret_cast<const uint4*>(al + static_cast<size_t>(j) * I + (c << 5));
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float4 t4 = ap[v];
-          af[4 * v] = t4.x; af[4 * v + 1] = t4.y; af[4 * v + 2] = t4.z; af[4 * v + 3] = t4.w;
+        for (int v = 0; v < 4; ++v) {
+          const uint4 th = hp[v], tl = lp[v];
+          hw[4 * v] = th.x; hw[4 * v + 1] = th.y; hw[4 * v + 2] = th.z; hw[4 * v + 3] = th.w;
+          lw[4 * v] = tl.x; lw[4 * v + 1] = tl.y; lw[4 * v + 2] = tl.z; lw[4 * v + 3] = tl.w;
         }
         float sa = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 32; ++v) sa += af[v];
+        for (int v = 0; v < 16; ++v) sa = dot2_bf16(lw[v], 0x3F803F80u, dot2_bf16(hw[v], 0x3F803F80u, sa));
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
           const int m = slot + i * slots;
@@ -233,10 +274,13 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
             float d = 0.0f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              float qf[8];
-              unpack8_f32(w4[v], qf);
+              uint32_t p[4];
+              unpack8_bias128_m(w4[v], nib_mask, p);
 #pragma unroll
-              for (int e8 = 0; e8 < 8; ++e8) d = fmaf(af[8 * v + e8], qf[e8], d);
+              for (int e8 = 0; e8 < 4; ++e8) {
+                d = dot2_bf16(p[e8], hw[4 * v + e8], d);
+                d = dot2_bf16(p[e8], lw[4 * v + e8], d);
+              }
             }
             acc[i] = fmaf(wr[u] * ss[si], fmaf(-zs[si], sa, d), acc[i]);
           }
@@ -273,16 +317,22 @@ int grid_for(int work_groups, int max_workgroups) {
 }
 
 size_t down_lds(int I, int k, int g) {
-  return sizeof(float) * (static_cast<size_t>(k) * I + 2 * static_cast<size_t>(k) * kDownRows * (I / g)) +
-         sizeof(int) * static_cast<size_t>(k);
+  return sizeof(uint16_t) * 2 * static_cast<size_t>(k) * I +
+         sizeof(float) * 2 * static_cast<size_t>(k) * kDownRows * (I / g);
+}
+
+int log2_of(int g) {
+  int s = 0;
+  while ((1 << s) < g) ++s;
+  return s;
 }
 
 template <int kKpw, int kRps>
 void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
   hipLaunchKernelGGL((decode_down_int4<kKpw, kRps>), dim3(wgs), dim3(kDownThreads),
-                     down_lds(p.I, p.k, p.w2.group), stream, p.a, p.ids, p.topk_w,
+                     down_lds(p.I, p.k, p.w2.group), stream, p.a_hi, p.a_lo, p.ids, p.topk_w,
                      static_cast<const uint32_t*>(p.w2.q), static_cast<const uint16_t*>(p.w2.scale),
-                     p.w2.zero, p.y, p.M, p.k, p.E, p.H, p.I, p.w2.group);
+                     p.w2.zero, p.y, p.M, p.k, p.E, p.H, p.I, log2_of(p.w2.group));
 }
 
 template <int kKpw>
@@ -300,10 +350,12 @@ void launch_down_rps(const DecodeArgs& p, int wgs, hipStream_t stream) {
 }  // namespace
 
 bool decode_shape_ok(int H, int I, int k, int g13, int g2) {
-  // Two 32-element chunks of a down row per lane at most (I <= 4096), and the
-  // staged intermediate rows of one token fit in LDS.
-  (void)g13;
-  return (H % 32) == 0 && (I % 32) == 0 && I <= 4096 && (I % kNpw) == 0 &&
+  // Two 32-element chunks of a down row per lane at most (I <= 4096), the
+  // staged intermediate rows of one token fit in LDS, and the W13 group is a
+  // power of two (the gate/up kernel divides by shifting).
+  return (H % 32) == 0 && (I % 32) == 0 && I <= 4096 && (I % kNpw) == 0 && (g13 & (g13 - 1)) == 0 &&
+         H / g13 <= kMaxGroups &&
+         (g2 & (g2 - 1)) == 0 &&
          (H % kDownRows) == 0 && k >= 1 && k <= 2 * kDownWaves && down_lds(I, k, g2) <= kMaxDownLds;
 }
 
@@ -313,7 +365,7 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const int wgs = grid_for((waves + kGateUpWaves - 1) / kGateUpWaves, p.max_workgroups);
   hipLaunchKernelGGL(decode_gate_up_int4, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids,
                      static_cast<const uint32_t*>(p.w13.q), static_cast<const uint16_t*>(p.w13.scale),
-                     p.w13.zero, p.a, mk, p.k, p.E, p.H, p.I, p.w13.group);
+                     p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H, p.I, log2_of(p.w13.group));
   return hipGetLastError();
 }
 

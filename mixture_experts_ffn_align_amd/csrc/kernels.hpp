@@ -20,8 +20,9 @@ struct DecodeArgs {
   const int32_t* ids;
   const float* topk_w;
   moe_weights w13, w2;
-  float* a;  // fp32 [M*k][I]
-  float* y;  // fp32 [M][H]
+  uint16_t* a_hi;  // bf16 [M*k][I] intermediate, high part
+  uint16_t* a_lo;  // bf16 [M*k][I] intermediate, low part
+  float* y;        // fp32 [M][H]
   int M, H, I, E, k;
   int max_workgroups;
 };
