@@ -17,15 +17,15 @@
 //   row; silu(gate) * up goes to the intermediate as a bf16 hi/lo pair
 //   (a = hi + lo to within 2^-17 relative).
 // Kernel 2 (down + combine): a workgroup owns kDownRows hidden outputs of
-//   one token; wave w streams the down rows of routes j = w, w+8, ... and
-//   folds the routing weight into its fp32 accumulators. The token's
-//   intermediate rows (hi and lo planes) and the tile's scales and zeros are
-//   staged in LDS; the weights are again bf16 (128 + q) pairs and each pair
-//   is dotted with the hi and the lo plane.
-//   Lanes of a wave form slots of pow2(I/32) lanes; a slot owns some of the
-//   rows and its lanes cover the I/32 chunks. The eight wave partials are
-//   added in wave (= route) order and y is written once. No floating-point
-//   atomics anywhere.
+//   one token; wave w takes the routes j = w, w+8, ... and folds the routing
+//   weight into its fp32 accumulators. Lanes of a wave form slots of
+//   pow2(I/32) lanes; a slot owns some of the rows and its lanes cover the
+//   I/32 chunks. Each lane loads its intermediate chunks (hi and lo planes)
+//   straight into registers, then its weight words, scales and zeros, so a
+//   route costs a single wait on memory; the weights are bf16 (128 + q)
+//   pairs, each dotted with the hi and the lo plane. The eight wave partials
+//   are added in wave order and y is written once. No floating-point atomics
+//   anywhere.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,8 +39,6 @@ constexpr int kNpw = 2;                       // neurons per wave
 constexpr int kDownWaves = 8;
 constexpr int kDownThreads = kDownWaves * kWave;
 constexpr int kDownRows = 8;
-constexpr size_t kMaxDownLds = 48 * 1024;     // staged intermediate rows + scales + zeros
-constexpr int kMaxGroups = 32;                // scale groups per row held in LDS (K / g)
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
@@ -67,9 +65,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
     const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
     int mk, int k, int E, int H, int I, int g_shift) {
-  __shared__ float2 wsz[kGateUpWaves][2 * kNpw * kMaxGroups];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave_l = uniform(threadIdx.x / kWave);
   // Task indices are wave-uniform: keep them (and the row addresses) scalar.
   const int wave_id = uniform(blockIdx.x * kGateUpWaves + threadIdx.x / kWave);
   const int nwaves = gridDim.x * kGateUpWaves;
@@ -104,12 +100,6 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     float acc[2 * kNpw];
 #pragma unroll
     for (int j = 0; j < 2 * kNpw; ++j) acc[j] = 0.0f;
-    // The rows' scales and zeros: one coalesced load per lane into this
-    // wave's LDS slice (a wave reads back only what it wrote, so no barrier).
-    for (int v = lane; v < 2 * kNpw * gpr; v += kWave) {
-      const int j = v / gpr, gi = v - j * gpr;
-      wsz[wave_l][v] = make_float2(half_bits_to_float(srow[j][gi]), 128.0f + static_cast<float>(zrow[j][gi]));
-    }
     const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
     for (int c = lane; c < nch; c += kWave) {
       // Issue the weight loads first so they are all in flight together.
@@ -118,11 +108,13 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
       const int grp = (c << 5) >> g_shift;
 #pragma unroll
       for (int j = 0; j < 2 * kNpw; ++j) wv[j] = load_stream16(qrow[j] + 4 * c);
+      uint32_t sv[2 * kNpw], zv[2 * kNpw];
+#pragma unroll
+      for (int j = 0; j < 2 * kNpw; ++j) { sv[j] = srow[j][grp]; zv[j] = zrow[j][grp]; }
 #pragma unroll
       for (int j = 0; j < 2 * kNpw; ++j) {
-        const float2 sz = wsz[wave_l][j * gpr + grp];
-        s[j] = sz.x;
-        zb[j] = sz.y;
+        s[j] = half_bits_to_float(static_cast<uint16_t>(sv[j]));
+        zb[j] = 128.0f + static_cast<float>(zv[j]);
       }
       uint32_t xw[16];
 #pragma unroll
@@ -164,26 +156,21 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
   }
 }
 
-// kRps: rows per lane, ceil(kDownRows / slots); kKpw: routes per wave.
-template <int kKpw, int kRps>
+// kCh: 32-element chunks of a down row per lane (1 or 2); kRps: rows per
+// lane, ceil(kDownRows / slots). Routes j = wave, wave + 8 are taken in turn.
+template <int kCh, int kRps>
 __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
     const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
     const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
     const uint8_t* __restrict__ zp, float* __restrict__ y, int M, int k, int E, int H, int I,
     int g_shift) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int gpr = I >> g_shift;
-  uint16_t* ah = reinterpret_cast<uint16_t*>(lds);                          // [k][I] hi plane
-  uint16_t* al = ah + static_cast<size_t>(k) * I;                           // [k][I] lo plane
-  float* ss = reinterpret_cast<float*>(al + static_cast<size_t>(k) * I);    // [k][kDownRows][gpr]
-  float* zs = ss + k * kDownRows * gpr;                                     // 128 + zero
   __shared__ float part[kDownWaves][kDownRows];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
   const int tiles_per_tok = H / kDownRows;
   const int ntiles = M * tiles_per_tok;
-  const int nch = I >> 5, words = I >> 3;
+  const int nch = I >> 5, words = I >> 3, gpr = I >> g_shift;
   int span = 1;
   while (span < nch && span < kWave) span <<= 1;
   const int slots = kWave / span;
@@ -194,74 +181,67 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t = tile / tiles_per_tok;
     const int h0 = (tile - t * tiles_per_tok) * kDownRows;
-    int ex[kKpw];
-    float wr[kKpw];
+    float acc[kRps];
 #pragma unroll
-    for (int u = 0; u < kKpw; ++u) {
-      const int j = wave + kDownWaves * u;
-      ex[u] = j < k ? uniform(load_expert(ids, t * k + j, E)) : -1;
-      wr[u] = j < k ? topk_w[t * k + j] : 0.0f;
-    }
-    // Weight loads of this wave's routes (two chunks per lane at most).
-    constexpr int kMaxCh = 2;
-    uint4 wv[kKpw][kMaxCh][kRps];
+    for (int i = 0; i < kRps; ++i) acc[i] = 0.0f;
+    for (int j = wave; j < k; j += kDownWaves) {
+      // Every load of this route is issued before the first wait: the
+      // intermediate chunks (they do not depend on the expert id), then the
+      // packed weights, then the scales and zeros.
+      const size_t r = static_cast<size_t>(t) * k + j;
+      uint4 hv[kCh][4], lv[kCh][4];
 #pragma unroll
-    for (int u = 0; u < kKpw; ++u) {
-      if (ex[u] < 0) continue;
-      const uint32_t* qt = q + (static_cast<size_t>(ex[u]) * H + h0) * words;
+      for (int cc = 0; cc < kCh; ++cc) {
+        const int c = c0 + cc * span;
+        if (c >= nch) continue;
+        const uint4* hp = reinterpret_cast<const uint4*>(a_hi + r * I + (c << 5));
+        const uint4* lp = reinterpret_cast<const uint4*>(a_lo + r * I + (c << 5));
 #pragma unroll
-      for (int cc = 0; cc < kMaxCh; ++cc) {
+        for (int v = 0; v < 4; ++v) { hv[cc][v] = hp[v]; lv[cc][v] = lp[v]; }
+      }
+      const int e = uniform(load_expert(ids, static_cast<int>(r), E));
+      if (e < 0) continue;
+      const float wr = topk_w[r];
+      const uint32_t* qt = q + (static_cast<size_t>(e) * H + h0) * words;
+      const size_t gt = (static_cast<size_t>(e) * H + h0) * gpr;
+      uint4 wv[kCh][kRps];
+      uint32_t sv[kCh][kRps], zv[kCh][kRps];
+#pragma unroll
+      for (int cc = 0; cc < kCh; ++cc) {
         const int c = c0 + cc * span;
         if (c >= nch) continue;
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
           const int m = slot + i * slots;
-          if (m < kDownRows) wv[u][cc][i] = load_stream16(qt + m * words + 4 * c);
+          if (m < kDownRows) wv[cc][i] = load_stream16(qt + m * words + 4 * c);
         }
       }
-    }
-    // Stage the token's intermediate rows, and the tile's scales and zeros.
-    const uint4* gh = reinterpret_cast<const uint4*>(a_hi + static_cast<size_t>(t) * k * I);
-    const uint4* gl = reinterpret_cast<const uint4*>(a_lo + static_cast<size_t>(t) * k * I);
-    for (int v = threadIdx.x; v < k * I / 8; v += kDownThreads) {
-      reinterpret_cast<uint4*>(ah)[v] = gh[v];
-      reinterpret_cast<uint4*>(al)[v] = gl[v];
-    }
-    // Each wave stages the scales and zeros of its own routes' rows (one
-    // coalesced load per lane); it is the only reader of that slice.
 #pragma unroll
-    for (int u = 0; u < kKpw; ++u) {
-      if (ex[u] < 0) continue;
-      const int j = wave + kDownWaves * u;
-      const size_t base = (static_cast<size_t>(ex[u]) * H + h0) * gpr;
-      for (int v = lane; v < kDownRows * gpr; v += kWave) {
-        ss[j * kDownRows * gpr + v] = half_bits_to_float(sc[base + v]);
-        zs[j * kDownRows * gpr + v] = 128.0f + static_cast<float>(zp[base + v]);
-      }
-    }
-    __syncthreads();
-
-    float acc[kRps];
-#pragma unroll
-    for (int i = 0; i < kRps; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kKpw; ++u) {
-      if (ex[u] < 0) continue;
-      const int j = wave + kDownWaves * u;
-#pragma unroll
-      for (int cc = 0; cc < kMaxCh; ++cc) {
+      for (int cc = 0; cc < kCh; ++cc) {
         const int c = c0 + cc * span;
         if (c >= nch) continue;
         const int grp = (c << 5) >> g_shift;
-        uint32_t hw[16], lw[16];
-        const uint4* hp = reinterpret_cast<const uint4*>(ah + static_cast<size_t>(j) * I + (c << 5));
-        const uint4* lp = reinterpret_cast<const uint4*>(al + static_cast<size_t>(j) * I + (c << 5));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 th = hp[v], tl = lp[v];
-          hw[4 * v] = th.x; hw[4 * v + 1] = th.y; hw[4 * v + 2] = th.z; hw[4 * v + 3] = th.w;
-          lw[4 * v] = tl.x; lw[4 * v + 1] = tl.y; lw[4 * v + 2] = tl.z; lw[4 * v + 3] = tl.w;
+        for (int i = 0; i < kRps; ++i) {
+          const int m = slot + i * slots;
+          if (m < kDownRows) {
+            sv[cc][i] = sc[gt + m * gpr + grp];
+            zv[cc][i] = zp[gt + m * gpr + grp];
+          }
         }
+      }
+#pragma unroll
+      for (int cc = 0; cc < kCh; ++cc) {
+        const int c = c0 + cc * span;
+        if (c >= nch) continue;
+        const uint32_t hw[16] = {hv[cc][0].x, hv[cc][0].y, hv[cc][0].z, hv[cc][0].w,
+                                 hv[cc][1].x, hv[cc][1].y, hv[cc][1].z, hv[cc][1].w,
+                                 hv[cc][2].x, hv[cc][2].y, hv[cc][2].z, hv[cc][2].w,
+                                 hv[cc][3].x, hv[cc][3].y, hv[cc][3].z, hv[cc][3].w};
+        const uint32_t lw[16] = {lv[cc][0].x, lv[cc][0].y, lv[cc][0].z, lv[cc][0].w,
+                                 lv[cc][1].x, lv[cc][1].y, lv[cc][1].z, lv[cc][1].w,
+                                 lv[cc][2].x, lv[cc][2].y, lv[cc][2].z, lv[cc][2].w,
+                                 lv[cc][3].x, lv[cc][3].y, lv[cc][3].z, lv[cc][3].w};
         float sa = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) sa = dot2_bf16(lw[v], 0x3F803F80u, dot2_bf16(hw[v], 0x3F803F80u, sa));
@@ -269,8 +249,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
         for (int i = 0; i < kRps; ++i) {
           const int m = slot + i * slots;
           if (m < kDownRows) {
-            const int si = (j * kDownRows + m) * gpr + grp;
-            const uint32_t w4[4] = {wv[u][cc][i].x, wv[u][cc][i].y, wv[u][cc][i].z, wv[u][cc][i].w};
+            const uint32_t w4[4] = {wv[cc][i].x, wv[cc][i].y, wv[cc][i].z, wv[cc][i].w};
             float d = 0.0f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -282,7 +261,9 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
                 d = dot2_bf16(p[e8], lw[4 * v + e8], d);
               }
             }
-            acc[i] = fmaf(wr[u] * ss[si], fmaf(-zs[si], sa, d), acc[i]);
+            const float s = half_bits_to_float(static_cast<uint16_t>(sv[cc][i]));
+            const float zb = 128.0f + static_cast<float>(zv[cc][i]);
+            acc[i] = fmaf(wr * s, fmaf(-zb, sa, d), acc[i]);
           }
         }
       }
@@ -316,47 +297,41 @@ int grid_for(int work_groups, int max_workgroups) {
   return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : work_groups;
 }
 
-size_t down_lds(int I, int k, int g) {
-  return sizeof(uint16_t) * 2 * static_cast<size_t>(k) * I +
-         sizeof(float) * 2 * static_cast<size_t>(k) * kDownRows * (I / g);
-}
-
 int log2_of(int g) {
   int s = 0;
   while ((1 << s) < g) ++s;
   return s;
 }
 
-template <int kKpw, int kRps>
+template <int kCh, int kRps>
 void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_down_int4<kKpw, kRps>), dim3(wgs), dim3(kDownThreads),
-                     down_lds(p.I, p.k, p.w2.group), stream, p.a_hi, p.a_lo, p.ids, p.topk_w,
-                     static_cast<const uint32_t*>(p.w2.q), static_cast<const uint16_t*>(p.w2.scale),
-                     p.w2.zero, p.y, p.M, p.k, p.E, p.H, p.I, log2_of(p.w2.group));
+  hipLaunchKernelGGL((decode_down_int4<kCh, kRps>), dim3(wgs), dim3(kDownThreads), 0, stream,
+                     p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const uint32_t*>(p.w2.q),
+                     static_cast<const uint16_t*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E, p.H,
+                     p.I, log2_of(p.w2.group));
 }
 
-template <int kKpw>
+template <int kCh>
 void launch_down_rps(const DecodeArgs& p, int wgs, hipStream_t stream) {
   int nch = p.I >> 5, span = 1;
   while (span < nch && span < kWave) span <<= 1;
   const int slots = kWave / span;
   const int rps = (kDownRows + slots - 1) / slots;
-  if (rps <= 1) launch_down<kKpw, 1>(p, wgs, stream);
-  else if (rps <= 2) launch_down<kKpw, 2>(p, wgs, stream);
-  else if (rps <= 4) launch_down<kKpw, 4>(p, wgs, stream);
-  else launch_down<kKpw, 8>(p, wgs, stream);
+  if (rps <= 1) launch_down<kCh, 1>(p, wgs, stream);
+  else if (rps <= 2) launch_down<kCh, 2>(p, wgs, stream);
+  else if (rps <= 4) launch_down<kCh, 4>(p, wgs, stream);
+  else launch_down<kCh, 8>(p, wgs, stream);
 }
 
 }  // namespace
 
 bool decode_shape_ok(int H, int I, int k, int g13, int g2) {
-  // Two 32-element chunks of a down row per lane at most (I <= 4096), the
-  // staged intermediate rows of one token fit in LDS, and the W13 group is a
-  // power of two (the gate/up kernel divides by shifting).
+  // Two 32-element chunks of a down row per lane at most (I <= 4096), at most
+  // two routes per down wave (k <= 16), and power-of-two groups (the kernels
+  // divide by shifting).
   return (H % 32) == 0 && (I % 32) == 0 && I <= 4096 && (I % kNpw) == 0 && (g13 & (g13 - 1)) == 0 &&
-         H / g13 <= kMaxGroups &&
          (g2 & (g2 - 1)) == 0 &&
-         (H % kDownRows) == 0 && k >= 1 && k <= 2 * kDownWaves && down_lds(I, k, g2) <= kMaxDownLds;
+         (H % kDownRows) == 0 && k >= 1 && k <= 2 * kDownWaves;
 }
 
 hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
@@ -371,7 +346,7 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
 
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream) {
   const int wgs = grid_for(p.M * (p.H / kDownRows), p.max_workgroups);
-  if (p.k <= kDownWaves) launch_down_rps<1>(p, wgs, stream);
+  if ((p.I >> 5) <= kWave) launch_down_rps<1>(p, wgs, stream);
   else launch_down_rps<2>(p, wgs, stream);
   return hipGetLastError();
 }
