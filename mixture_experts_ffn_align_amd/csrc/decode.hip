@@ -111,6 +111,12 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
       uint32_t sv[2 * kNpw], zv[2 * kNpw];
 #pragma unroll
       for (int j = 0; j < 2 * kNpw; ++j) { sv[j] = srow[j][grp]; zv[j] = zrow[j][grp]; }
+      uint4 xv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xv[v] = xrow[c * 4 + v];
+      // Keep every load above this point: the scheduler would otherwise sink
+      // some of them below the first use of the others and add a round trip.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 2 * kNpw; ++j) {
         s[j] = half_bits_to_float(static_cast<uint16_t>(sv[j]));
@@ -119,8 +125,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
       uint32_t xw[16];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint4 t4 = xrow[c * 4 + v];
-        xw[4 * v] = t4.x; xw[4 * v + 1] = t4.y; xw[4 * v + 2] = t4.z; xw[4 * v + 3] = t4.w;
+        xw[4 * v] = xv[v].x; xw[4 * v + 1] = xv[v].y; xw[4 * v + 2] = xv[v].z; xw[4 * v + 3] = xv[v].w;
       }
       float sx = 0.0f;
 #pragma unroll
@@ -156,27 +161,46 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
   }
 }
 
-// kCh: 32-element chunks of a down row per lane (1 or 2); kRps: rows per
-// lane, ceil(kDownRows / slots). Routes j = wave, wave + 8 are taken in turn.
-template <int kCh, int kRps>
+// kSpan: lanes per slot, pow2(I/32) capped at 64; kCh: 32-element chunks of
+// a down row per lane (1, or 2 when I/32 > 64). Routes j = wave, wave + 8, ...
+// are taken in turn.
+template <int kCh, int kSpan>
 __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
     const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
     const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
     const uint8_t* __restrict__ zp, float* __restrict__ y, int M, int k, int E, int H, int I,
     int g_shift) {
+  constexpr int kSlots = kWave / kSpan;
+  constexpr int kRps = (kDownRows + kSlots - 1) / kSlots;  // rows per lane
   __shared__ float part[kDownWaves][kDownRows];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
   const int tiles_per_tok = H / kDownRows;
   const int ntiles = M * tiles_per_tok;
   const int nch = I >> 5, words = I >> 3, gpr = I >> g_shift;
-  int span = 1;
-  while (span < nch && span < kWave) span <<= 1;
-  const int slots = kWave / span;
-  const int slot = lane / span;
-  const int c0 = lane - slot * span;
+  const int span = kSpan, slots = kSlots;
+  const int slot = lane / kSpan;
+  const int c0 = lane - slot * kSpan;
   const uint32_t nib_mask = in_vgpr(0x000F000Fu);
+
+  // Lanes past the last chunk, and slots past the last row (tiny I), read a
+  // clamped in-bounds address and contribute zero: the loop body has no
+  // per-lane branches, so the row chains can be interleaved.
+  int cl[kCh];
+  float cvalid[kCh];
+#pragma unroll
+  for (int cc = 0; cc < kCh; ++cc) {
+    const int c = c0 + cc * span;
+    cl[cc] = c < nch ? c : 0;
+    cvalid[cc] = (c < nch && slot < kDownRows) ? 1.0f : 0.0f;
+  }
+  int mrow[kRps];
+#pragma unroll
+  for (int i = 0; i < kRps; ++i) {
+    const int m = slot + i * slots;
+    mrow[i] = m < kDownRows ? m : 0;
+  }
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t = tile / tiles_per_tok;
@@ -192,48 +216,41 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
       uint4 hv[kCh][4], lv[kCh][4];
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
-        const int c = c0 + cc * span;
-        if (c >= nch) continue;
-        const uint4* hp = reinterpret_cast<const uint4*>(a_hi + r * I + (c << 5));
-        const uint4* lp = reinterpret_cast<const uint4*>(a_lo + r * I + (c << 5));
+        const uint4* hp = reinterpret_cast<const uint4*>(a_hi + r * I + (cl[cc] << 5));
+        const uint4* lp = reinterpret_cast<const uint4*>(a_lo + r * I + (cl[cc] << 5));
 #pragma unroll
         for (int v = 0; v < 4; ++v) { hv[cc][v] = hp[v]; lv[cc][v] = lp[v]; }
       }
-      const int e = uniform(load_expert(ids, static_cast<int>(r), E));
-      if (e < 0) continue;
-      const float wr = topk_w[r];
+      // The scheduler must not move these loads below the expert-id wait,
+      // nor (further down) the weight loads below the first use of any load.
+      __builtin_amdgcn_sched_barrier(0);
+      // An invalid route has a zero intermediate (the gate/up kernel writes
+      // zeros for it); it reads expert 0's rows and adds exactly zero. No
+      // branch here: the compiler would sink the loads above into it.
+      const int e_raw = uniform(load_expert(ids, static_cast<int>(r), E));
+      const int e = e_raw < 0 ? 0 : e_raw;
+      const float wr = e_raw < 0 ? 0.0f : topk_w[r];
       const uint32_t* qt = q + (static_cast<size_t>(e) * H + h0) * words;
       const size_t gt = (static_cast<size_t>(e) * H + h0) * gpr;
       uint4 wv[kCh][kRps];
       uint32_t sv[kCh][kRps], zv[kCh][kRps];
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
-        const int c = c0 + cc * span;
-        if (c >= nch) continue;
 #pragma unroll
-        for (int i = 0; i < kRps; ++i) {
-          const int m = slot + i * slots;
-          if (m < kDownRows) wv[cc][i] = load_stream16(qt + m * words + 4 * c);
-        }
+        for (int i = 0; i < kRps; ++i) wv[cc][i] = load_stream16(qt + mrow[i] * words + 4 * cl[cc]);
       }
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
-        const int c = c0 + cc * span;
-        if (c >= nch) continue;
-        const int grp = (c << 5) >> g_shift;
+        const int grp = (cl[cc] << 5) >> g_shift;
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
-          const int m = slot + i * slots;
-          if (m < kDownRows) {
-            sv[cc][i] = sc[gt + m * gpr + grp];
-            zv[cc][i] = zp[gt + m * gpr + grp];
-          }
+          sv[cc][i] = sc[gt + mrow[i] * gpr + grp];
+          zv[cc][i] = zp[gt + mrow[i] * gpr + grp];
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
-        const int c = c0 + cc * span;
-        if (c >= nch) continue;
         const uint32_t hw[16] = {hv[cc][0].x, hv[cc][0].y, hv[cc][0].z, hv[cc][0].w,
                                  hv[cc][1].x, hv[cc][1].y, hv[cc][1].z, hv[cc][1].w,
                                  hv[cc][2].x, hv[cc][2].y, hv[cc][2].z, hv[cc][2].w,
@@ -242,44 +259,68 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
                                  lv[cc][1].x, lv[cc][1].y, lv[cc][1].z, lv[cc][1].w,
                                  lv[cc][2].x, lv[cc][2].y, lv[cc][2].z, lv[cc][2].w,
                                  lv[cc][3].x, lv[cc][3].y, lv[cc][3].z, lv[cc][3].w};
-        float sa = 0.0f;
+        // Sum of the chunk's activations in four independent chains.
+        float sa4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sa = dot2_bf16(lw[v], 0x3F803F80u, dot2_bf16(hw[v], 0x3F803F80u, sa));
+        for (int v = 0; v < 16; ++v)
+          sa4[v & 3] = dot2_bf16(lw[v], 0x3F803F80u, dot2_bf16(hw[v], 0x3F803F80u, sa4[v & 3]));
+        const float sa = (sa4[0] + sa4[1]) + (sa4[2] + sa4[3]);
+        // Per row, the hi and lo planes are separate chains.
+        float dh[kRps], dl[kRps];
+#pragma unroll
+        for (int i = 0; i < kRps; ++i) { dh[i] = 0.0f; dl[i] = 0.0f; }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+#pragma unroll
+          for (int i = 0; i < kRps; ++i) {
+            const uint32_t w = v == 0 ? wv[cc][i].x : v == 1 ? wv[cc][i].y : v == 2 ? wv[cc][i].z : wv[cc][i].w;
+            uint32_t p[4];
+            unpack8_bias128_m(w, nib_mask, p);
+#pragma unroll
+            for (int e8 = 0; e8 < 4; ++e8) {
+              dh[i] = dot2_bf16(p[e8], hw[4 * v + e8], dh[i]);
+              dl[i] = dot2_bf16(p[e8], lw[4 * v + e8], dl[i]);
+            }
+          }
+        }
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
-          const int m = slot + i * slots;
-          if (m < kDownRows) {
-            const uint32_t w4[4] = {wv[cc][i].x, wv[cc][i].y, wv[cc][i].z, wv[cc][i].w};
-            float d = 0.0f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              uint32_t p[4];
-              unpack8_bias128_m(w4[v], nib_mask, p);
-#pragma unroll
-              for (int e8 = 0; e8 < 4; ++e8) {
-                d = dot2_bf16(p[e8], hw[4 * v + e8], d);
-                d = dot2_bf16(p[e8], lw[4 * v + e8], d);
-              }
-            }
-            const float s = half_bits_to_float(static_cast<uint16_t>(sv[cc][i]));
-            const float zb = 128.0f + static_cast<float>(zv[cc][i]);
-            acc[i] = fmaf(wr * s, fmaf(-zb, sa, d), acc[i]);
-          }
+          const float s = cvalid[cc] * half_bits_to_float(static_cast<uint16_t>(sv[cc][i]));
+          const float zb = 128.0f + static_cast<float>(zv[cc][i]);
+          acc[i] = fmaf(wr * s, fmaf(-zb, sa, dh[i] + dl[i]), acc[i]);
         }
       }
     }
-    // Sum each row over the lanes of its slot (butterfly inside the span).
+    // Sum each row over the lanes of its slot: DPP butterflies inside 16-lane
+    // rows, then (slots wider than 16 lanes) the row sums read out in lane
+    // order. Fixed order, no LDS round trips.
 #pragma unroll
     for (int i = 0; i < kRps; ++i) {
       float v = acc[i];
-      for (int o = span >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+      if constexpr (kSpan > 1) v += dpp<0xB1>(v);   // xor 1
+      if constexpr (kSpan > 2) v += dpp<0x4E>(v);   // xor 2
+      if constexpr (kSpan > 4) v += dpp<0x141>(v);  // half-row mirror
+      if constexpr (kSpan > 8) v += dpp<0x140>(v);  // row mirror
       acc[i] = v;
     }
-    if (c0 == 0) {
+    if constexpr (kSpan <= 16) {
+      if (c0 == 0) {
+#pragma unroll
+        for (int i = 0; i < kRps; ++i) {
+          if (slot + i * kSlots < kDownRows) part[wave][slot + i * kSlots] = acc[i];
+        }
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < kRps; ++i) {
-        const int m = slot + i * slots;
-        if (m < kDownRows) part[wave][m] = acc[i];
+#pragma unroll
+        for (int sl = 0; sl < kSlots; ++sl) {
+          float v = 0.0f;
+#pragma unroll
+          for (int rr = 0; rr < kSpan / 16; ++rr)
+            v += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[i]), sl * kSpan + 16 * rr));
+          if (lane == 0) part[wave][sl + i * kSlots] = v;
+        }
       }
     }
     __syncthreads();
@@ -303,24 +344,12 @@ int log2_of(int g) {
   return s;
 }
 
-template <int kCh, int kRps>
+template <int kCh, int kSpan>
 void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_down_int4<kCh, kRps>), dim3(wgs), dim3(kDownThreads), 0, stream,
+  hipLaunchKernelGGL((decode_down_int4<kCh, kSpan>), dim3(wgs), dim3(kDownThreads), 0, stream,
                      p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const uint32_t*>(p.w2.q),
                      static_cast<const uint16_t*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E, p.H,
                      p.I, log2_of(p.w2.group));
-}
-
-template <int kCh>
-void launch_down_rps(const DecodeArgs& p, int wgs, hipStream_t stream) {
-  int nch = p.I >> 5, span = 1;
-  while (span < nch && span < kWave) span <<= 1;
-  const int slots = kWave / span;
-  const int rps = (kDownRows + slots - 1) / slots;
-  if (rps <= 1) launch_down<kCh, 1>(p, wgs, stream);
-  else if (rps <= 2) launch_down<kCh, 2>(p, wgs, stream);
-  else if (rps <= 4) launch_down<kCh, 4>(p, wgs, stream);
-  else launch_down<kCh, 8>(p, wgs, stream);
 }
 
 }  // namespace
@@ -346,8 +375,16 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
 
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream) {
   const int wgs = grid_for(p.M * (p.H / kDownRows), p.max_workgroups);
-  if ((p.I >> 5) <= kWave) launch_down_rps<1>(p, wgs, stream);
-  else launch_down_rps<2>(p, wgs, stream);
+  const int nch = p.I >> 5;
+  if (nch > 32) {
+    if (nch > kWave) launch_down<2, 64>(p, wgs, stream);
+    else launch_down<1, 64>(p, wgs, stream);
+  } else if (nch > 16) launch_down<1, 32>(p, wgs, stream);
+  else if (nch > 8) launch_down<1, 16>(p, wgs, stream);
+  else if (nch > 4) launch_down<1, 8>(p, wgs, stream);
+  else if (nch > 2) launch_down<1, 4>(p, wgs, stream);
+  else if (nch > 1) launch_down<1, 2>(p, wgs, stream);
+  else launch_down<1, 1>(p, wgs, stream);
   return hipGetLastError();
 }
 

@@ -59,6 +59,12 @@ RAGGED = [
     dict(M=9, H=2048, I=768, E=128, k=8, b=64, g=128),
     dict(M=5, H=256, I=128, E=1, k=1, b=8, g=32),
     dict(M=20, H=384, I=2176, E=4, k=2, b=8, g=128),     # I/32 = 68 chunks > 64 lanes
+    # Decode down-kernel lane layouts: one chunk per row (I=32), two (I=64),
+    # 14 (16-lane slots), 48 (one 64-lane slot); k > 8 gives a wave two routes.
+    dict(M=4, H=128, I=32, E=4, k=2, b=8, g=32),
+    dict(M=3, H=192, I=64, E=8, k=3, b=8, g=32),
+    dict(M=2, H=320, I=448, E=16, k=5, b=8, g=64),
+    dict(M=2, H=256, I=1536, E=16, k=12, b=8, g=128),
 ]
 
 
