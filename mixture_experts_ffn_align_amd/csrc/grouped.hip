@@ -5,30 +5,36 @@
 // Section 3.4: grouped GEMM over routing-dependent token counts, weights as
 // the left operand so Y_e^T = W_e X_e^T).
 //
-// A workgroup takes one aligned block (b <= 64 routes of one expert, four
-// 16-token sub-tiles) and 64 output rows; wave w owns rows 16w..16w+15.
-// Every GEMM uses v_mfma_f32_16x16x32_bf16 with the expert's weight rows on
-// the A operand and the block's tokens on B:
+// One kernel template serves both GEMMs. A workgroup takes one aligned block
+// (b <= 64 routes of one expert: four 16-column sub-tiles) and 64 output rows;
+// wave w owns rows 16w..16w+15 (for gate/up: those 16 neurons' gate rows and
+// their up rows). Every product is v_mfma_f32_16x16x32_bf16 with the expert's
+// weight rows on A and the block's columns on B:
 //   A lane l: weight row l%16, 8 reduction elements of lane group l/16;
-//   B lane l: token column l%16, the same 8 reduction elements;
+//   B lane l: column l%16, the same 8 reduction elements;
 //   D lane l: rows 4*(l/16)+i (i < 4) of column l%16.
-// The reduction runs in slabs of 32*kSpw elements, each inside one
-// quantisation group; lane group q holds words kSpw*q .. kSpw*q+kSpw-1 of a
-// slab row and MFMA step j uses word kSpw*q + j. The block's activations for
-// a slab are staged in LDS (double-buffered: the next slab's global loads
-// are in flight while the current slab's MFMAs run) and shared by the four
-// waves; each wave streams only its own weight rows, one slab ahead, straight
-// into registers. Sub-tiles with no valid route are skipped.
+// The reduction runs in slabs of 128 elements, four MFMA steps of 32 each
+// (step j, lane group q: elements 32j+8q .. 32j+8q+7 of the slab), so every
+// step lies inside one quantisation group whenever g is a multiple of 32.
 //
-// gate/up: the int4 words become bf16 (128 + q) pairs with one AND-OR (AWQ
-//   nibble order) and a second MFMA per step adds -(128 + z) times the same
-//   activations, so each slab's accumulator holds sum x (q - z) for the
-//   group; it is scaled by the group scale in fp32. The epilogue writes
-//   silu(gate) * up for every valid route as a bf16 hi/lo pair (a = hi + lo
-//   to within 2^-17 relative), the B operand of the down GEMM.
-// down: the weights are dequantised exactly to bf16 integers (q - z lies in
-//   [-15, 15]) and two MFMAs per step take the hi and lo planes of the
-//   intermediate. Each route's yhat row is written once.
+// Data movement: the weight rows of a wave (16 rows x 64 bytes per slab and
+// row set) and the block's activation rows (16 bytes per lane, per sub-tile,
+// step and plane) go global -> LDS with 16-byte LDS-DMA loads into rings of
+// kD slabs, issued kD-1 slabs ahead; nothing passes through VGPRs. Each
+// slab costs one wait on the wave's own loads (an exact vmcnt: the loads of
+// the later slabs stay in flight) and one workgroup barrier. The activation
+// loads of a slab are spread evenly over the four waves and cover only
+// sub-tiles that hold a valid route; the tile's scales and zeros arrive with
+// the first slab. Sub-tiles with no valid route are skipped.
+//
+// The int4 words become bf16 (128 + q) pairs with one AND-OR each (AWQ
+// nibble order) and a second MFMA per step adds -(128 + z) times the same
+// activations, so a group's partial holds sum x (q - z); it is scaled by the
+// group scale in fp32.
+// gate/up: B is x; the epilogue writes silu(gate) * up for every valid route
+//   as a bf16 hi/lo pair (a = hi + lo to within 2^-17 relative).
+// down: B is the hi and the lo plane of the intermediate (both accumulate
+//   into the same partial); each route's yhat row is written once.
 // combine: y[t] = sum over j ascending of w[t,j] * yhat[t*k+j].
 // Workgroups whose block lies past num_padded (read on the device) exit at
 // once, so the grid can be sized from the host-known capacity. No
@@ -43,17 +49,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTileRows = 16 * kWaves;   // output rows per workgroup
-constexpr int kMaxTok = 64;              // block size limit: four 16-token sub-tiles
+constexpr int kMaxTok = 64;              // block size limit: four 16-column sub-tiles
 constexpr int kMaxSub = kMaxTok / 16;
+constexpr int kMaxGpr = 32;              // K / g limit (the tile's scales live in LDS)
 
 __device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // One packed word -> eight bf16 (128 + q), element order.
-__device__ __forceinline__ bf16x8 bias_pairs(uint32_t w) {
+__device__ __forceinline__ bf16x8 bias_pairs(uint32_t w, uint32_t m) {
   uint32_t p[4];
-  unpack8_bias128(w, p);
+  unpack8_bias128_m(w, m, p);
   return __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
 }
 
@@ -64,341 +71,355 @@ __device__ __forceinline__ bf16x8 neg_zero_pairs(uint32_t z) {
   return __builtin_bit_cast(bf16x8, make_uint4(pr, pr, pr, pr));
 }
 
-// One packed word -> eight exact bf16 values (q - z), element order.
-__device__ __forceinline__ bf16x8 dequant8_exact(uint32_t w, float z) {
-  float qf[8];
-  unpack8_f32(w, qf);
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(qf[i] - z);
-  return r;
+// LDS byte address of a __shared__ object (low half of its generic address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-template <int kSpw>
-__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[kSpw]) {
-  if constexpr (kSpw == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else if constexpr (kSpw == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
+// 16 bytes per lane from global memory to LDS at base + 16 * lane (LDS DMA).
+// M0 carries the LDS base; nothing else in these kernels uses M0.
+// It is issued from asm so that the compiler neither reorders it nor adds
+// waits for it; the kernel waits for these loads itself (wait_vm_le).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier for LDS data only. __syncthreads() also fences global
+// memory, which waits for every load in flight and would drain the rings.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Wait until at most about n vector-memory operations of this wave are in
+// flight (n wave-uniform, rounded down to 0..4, 6, 8, 12, 16 or 24: a
+// smaller count only waits longer). Loads complete in issue order, so this
+// waits for every load issued before the last n. A short branch tree keeps
+// the scalar work small.
+__device__ __forceinline__ void wait_vm_le(int n) {
+  if (n >= 8) {
+    if (n >= 16) {
+      if (n >= 24) wait_vm<24>(); else wait_vm<16>();
+    } else {
+      if (n >= 12) wait_vm<12>(); else wait_vm<8>();
+    }
+  } else if (n >= 4) {
+    if (n >= 6) wait_vm<6>(); else wait_vm<4>();
+  } else if (n >= 2) {
+    if (n >= 3) wait_vm<3>(); else wait_vm<2>();
   } else {
-    w[0] = p[0];
+    if (n >= 1) wait_vm<1>(); else wait_vm<0>();
   }
 }
 
-// Route of every column of the block (-1 for padding), staged in LDS, and
-// the per-lane view: route of column n of each sub-tile and which sub-tiles
-// hold a valid route.
-struct BlockView {
-  int rid[kMaxSub];
-  bool act[kMaxSub];
+struct GemmParams {
+  const uint16_t* b0;            // B rows (bf16, K per row): x [M] or a_hi [Mk]
+  const uint16_t* b1;            // second plane (a_lo) or null
+  const int32_t* sorted;
+  const int32_t* blocks;
+  const int32_t* num_padded;
+  const uint32_t* q;             // [E][rows_per_expert][K/8]
+  const uint16_t* sc;            // [E][rows_per_expert][K/g]
+  const uint8_t* zp;
+  uint16_t* a_hi;                // gate/up output planes [Mk][I]
+  uint16_t* a_lo;
+  float* yhat;                   // down output [Mk][H]
+  int mk, k, E, b, nblk;
+  int ntile;                     // tiles per block
+  int rows_per_expert;           // weight rows per expert (2I or H)
+  int set_stride;                // row offset of row set 1 (I: up rows; 64: next 64 rows)
+  int tile_stride;               // row offset between tiles (64 or 128)
+  int out_rows;                  // row length of the output (I or H)
+  int K, g;
 };
 
-__device__ __forceinline__ BlockView stage_block(const int32_t* sorted, int blk, int b, int mk,
-                                                 int* cols, int n) {
-  if (threadIdx.x < kMaxTok) {
-    int r = -1;
-    if (static_cast<int>(threadIdx.x) < b) {
-      r = sorted[static_cast<size_t>(blk) * b + threadIdx.x];
-      if (r < 0 || r >= mk) r = -1;
-    }
-    cols[threadIdx.x] = r;
-  }
-  __syncthreads();
-  BlockView v;
-#pragma unroll
-  for (int st = 0; st < kMaxSub; ++st) {
-    v.rid[st] = cols[16 * st + n];
-    v.act[st] = __ballot(v.rid[st] >= 0) != 0ull;
-  }
-  return v;
-}
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kRingBytes = 64 * 1024;
+constexpr int kMaxDepth = 8;
 
-// Weight words of a wave run kDepth slabs ahead of the MFMAs in a register
-// ring (the ring index is static: the slab loop is unrolled by kDepth), so
-// each wave keeps kDepth slabs of its weight rows in flight; kDepth * kSpw
-// words (256 reduction elements) per lane and row.
-#ifndef MOE_RING_WORDS
-#define MOE_RING_WORDS 4
-#endif
-template <int kSpw>
-constexpr int ring_depth() { return MOE_RING_WORDS / kSpw > 0 ? MOE_RING_WORDS / kSpw : 1; }
+// One workgroup of eight waves computes a tile of 2 x 64 weight rows against
+// one aligned block: wave w takes row set w / 4 (gate/up: the gate rows or
+// the up rows of 64 neurons; down: rows 0..63 or 64..127 of a 128-row tile),
+// rows 16 (w % 4) .. +15 of it.
+// kGateUp: epilogue silu(gate) * up (else yhat rows). kPlanes: B planes (1: x;
+// 2: the hi and lo planes). kSteps: 32-element MFMA steps per slab (4 or 2).
+// kFlush: steps per scaled partial (g / 32, at most kSteps).
+template <bool kGateUp, int kPlanes, int kSteps, int kFlush>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmParams p) {
+  constexpr int kSlabK = 32 * kSteps;                  // reduction elements per slab
+  constexpr int kRowBytes = kSlabK / 2;                // packed bytes per weight row and slab
+  constexpr int kRowsPerDma = 1024 / kRowBytes;        // weight rows per 1 KB LDS-DMA
+  constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row and slab
+  constexpr int kABytes = 2 * kTileRows * kRowBytes;   // weight bytes per slab (128 rows)
+  constexpr int kScStride = kTileRows * kMaxGpr * 2;   // bytes per row set (fp16 scales)
+  constexpr int kZpStride = kTileRows * kMaxGpr;       // bytes per row set (u8 zeros)
+  __shared__ __align__(16) unsigned char ring[kRingBytes];
+  __shared__ __align__(16) unsigned char ssh[2 * kScStride];
+  __shared__ __align__(16) unsigned char szz[2 * kZpStride];
+  __shared__ int cols[kMaxTok];    // route of each block column, -1 for padding
+  __shared__ int brow[kMaxTok];    // B row of each column (0 for padding)
 
-template <int kSpw>
-__global__ __launch_bounds__(kThreads) void grouped_gate_up_int4(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ blocks, const int32_t* __restrict__ num_padded,
-    const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
-    const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
-    int mk, int k, int E, int H, int I, int g, int b, int nblk) {
-  constexpr int kSlab = 32 * kSpw;
-  constexpr int kRowB = kSlab * 2 + 16;          // bytes per staged token row (padded)
-  constexpr int kChunks = kSlab / 8;             // 16-byte chunks per token row
-  constexpr int kMaxGroups = 64;                 // H / g held in LDS (H <= 8192 at g = 128)
-  constexpr int kDepth = ring_depth<kSpw>();
-  __shared__ __align__(16) unsigned char bs[2][kMaxTok * kRowB];
-  __shared__ uint16_t ssh[2 * kTileRows * kMaxGroups / 4];   // this tile's scales: [2*64 rows][gpr]
-  __shared__ uint8_t szz[2 * kTileRows * kMaxGroups / 4];    // and zeros
-  __shared__ int cols[kMaxTok];
-  __shared__ int toks[kMaxTok];                              // token of each block column, -1 if none
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform(threadIdx.x / kWave);
+  const int rs = wave >> 2;                         // this wave's row set
+  const int rl = 16 * (wave & 3);                   // first row of this wave within the set
   const int n = lane & 15, lq = lane >> 4;
-  const int ngroups = I / kTileRows;
-  const int ntasks = nblk * ngroups;
-  const int npad = num_padded[0];
-  const int words = H >> 3, gpr = H / g;
-  const int nslab = H / kSlab;
+  const int ntasks = p.nblk * p.ntile;
+  const int npad = p.num_padded[0];
+  const int words = p.K >> 3, gpr = p.K / p.g;
+  const int nslab = p.K / kSlabK;
+  const uint32_t nib_mask = in_vgpr(0x000F000Fu);
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-    const int blk = task / ngroups;
-    const int ng = task - blk * ngroups;
-    if (blk * b >= npad) continue;
-    const int e = blocks[blk];
-    if (e < 0 || e >= E) continue;
+    const int blk = task / p.ntile;
+    const int ng = task - blk * p.ntile;
+    if (blk * p.b >= npad) continue;
+    const int e = p.blocks[blk];
+    if (e < 0 || e >= p.E) continue;
 
-    // Weight rows of this wave: gate rows and up rows of 16 neurons.
-    const size_t tile0 = static_cast<size_t>(e) * (2 * I) + ng * kTileRows;
-    const size_t rowg = tile0 + wave * 16;
-    const size_t rowu = rowg + I;
-    const uint32_t* qg = q + (rowg + n) * words + kSpw * lq;
-    const uint32_t* qu = q + (rowu + n) * words + kSpw * lq;
-    uint32_t wg[kDepth][kSpw], wu[kDepth][kSpw];
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      if (d < nslab) {
-        load_words<kSpw>(qg + d * 4 * kSpw, wg[d]);
-        load_words<kSpw>(qu + d * 4 * kSpw, wu[d]);
-      }
-    }
-    // Scales and zeros of the tile's 64 gate and 64 up rows, for all groups.
-    for (int v = threadIdx.x; v < 2 * kTileRows * gpr; v += kThreads) {
-      const int half = v / (kTileRows * gpr);
-      const size_t off = (tile0 + half * static_cast<size_t>(I)) * gpr + (v - half * kTileRows * gpr);
-      ssh[v] = sc[off];
-      szz[v] = zp[off];
-    }
     if (threadIdx.x < kMaxTok) {
       const int c = threadIdx.x;
-      int r = c < b ? sorted[static_cast<size_t>(blk) * b + c] : -1;
-      toks[c] = (r >= 0 && r < mk) ? r / k : -1;
+      int r = -1;
+      if (c < p.b) {
+        r = p.sorted[static_cast<size_t>(blk) * p.b + c];
+        if (r < 0 || r >= p.mk) r = -1;
+      }
+      cols[c] = r;
+      brow[c] = r < 0 ? 0 : (kGateUp ? r / p.k : r);
     }
-    const BlockView bv = stage_block(sorted, blk, b, mk, cols, n);   // includes a barrier
-
-    uint4 breg[kSpw];
-    auto load_b = [&](int s) {
-#pragma unroll
-      for (int u = 0; u < kSpw; ++u) {
-        const int idx = threadIdx.x + kThreads * u;
-        const int col = idx / kChunks, ch = idx - col * kChunks;
-        const int t = toks[col];
-        breg[u] = t >= 0 ? *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + s * kSlab + ch * 8)
-                         : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto store_b = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < kSpw; ++u) {
-        const int idx = threadIdx.x + kThreads * u;
-        const int col = idx / kChunks, ch = idx - col * kChunks;
-        *reinterpret_cast<uint4*>(&bs[buf][col * kRowB + ch * 16]) = breg[u];
-      }
-    };
-
-    floatx4 accg[kMaxSub], accu[kMaxSub];
-#pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) { accg[st] = floatx4{0, 0, 0, 0}; accu[st] = floatx4{0, 0, 0, 0}; }
-
-    load_b(0);
-    store_b(0);
     __syncthreads();
-    const int lg = wave * 16 + n;               // local row of this lane's A operand
-    for (int s0 = 0; s0 < nslab; s0 += kDepth) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int s = s0 + d;
-        if (s >= nslab) break;
-        const int cur = s & 1;
-        const int grp = (s * kSlab) / g;
-        bf16x8 Ag[kSpw], Au[kSpw];
-#pragma unroll
-        for (int j = 0; j < kSpw; ++j) { Ag[j] = bias_pairs(wg[d][j]); Au[j] = bias_pairs(wu[d][j]); }
-        // Activation loads before the weight-ring loads: the wait before
-        // store_b then leaves the (later) weight loads in flight.
-        if (s + 1 < nslab) load_b(s + 1);
-        if (s + kDepth < nslab) {
-          load_words<kSpw>(qg + (s + kDepth) * 4 * kSpw, wg[d]);
-          load_words<kSpw>(qu + (s + kDepth) * 4 * kSpw, wu[d]);
-        }
-        const bf16x8 Zg = neg_zero_pairs(szz[lg * gpr + grp]);
-        const bf16x8 Zu = neg_zero_pairs(szz[(kTileRows + lg) * gpr + grp]);
-        float cg[4], cu[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cg[i] = half_bits_to_float(ssh[(wave * 16 + 4 * lq + i) * gpr + grp]);
-          cu[i] = half_bits_to_float(ssh[(kTileRows + wave * 16 + 4 * lq + i) * gpr + grp]);
-        }
-#pragma unroll
-        for (int st = 0; st < kMaxSub; ++st) {
-          if (!bv.act[st]) continue;
-          const unsigned char* brow = &bs[cur][(16 * st + n) * kRowB + 16 * kSpw * lq];
-          floatx4 dg = {0, 0, 0, 0}, du = {0, 0, 0, 0};
-#pragma unroll
-          for (int j = 0; j < kSpw; ++j) {
-            const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(brow + 16 * j));
-            dg = mfma_bf16(Ag[j], B, dg);
-            dg = mfma_bf16(Zg, B, dg);
-            du = mfma_bf16(Au[j], B, du);
-            du = mfma_bf16(Zu, B, du);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            accg[st][i] = fmaf(cg[i], dg[i], accg[st][i]);
-            accu[st][i] = fmaf(cu[i], du[i], accu[st][i]);
-          }
-        }
-        if (s + 1 < nslab) store_b(cur ^ 1);
-        __syncthreads();
-      }
-    }
+    // Active sub-tiles (wave-uniform), listed in order; static indices only,
+    // so the lists stay in registers.
+    int amask = 0;
 #pragma unroll
     for (int st = 0; st < kMaxSub; ++st) {
-      const int r = bv.rid[st];
-      if (r < 0) continue;
-      uint32_t hi2[2], lo2[2];
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const float v0 = silu_mul(accg[st][i], accu[st][i]);
-        const float v1 = silu_mul(accg[st][i + 1], accu[st][i + 1]);
-        const bf16x2 h = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
-        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-        const bf16x2 l = {static_cast<__bf16>(v0 - bf16_lo(hb)), static_cast<__bf16>(v1 - bf16_hi(hb))};
-        hi2[i / 2] = hb;
-        lo2[i / 2] = __builtin_bit_cast(uint32_t, l);
-      }
-      const size_t off = static_cast<size_t>(r) * I + ng * kTileRows + wave * 16 + 4 * lq;
-      *reinterpret_cast<uint2*>(a_hi + off) = make_uint2(hi2[0], hi2[1]);
-      *reinterpret_cast<uint2*>(a_lo + off) = make_uint2(lo2[0], lo2[1]);
+      if (__ballot(cols[16 * st + n] >= 0) != 0ull) amask |= 1 << st;
     }
-  }
-}
-
-template <int kSpw>
-__global__ __launch_bounds__(kThreads) void grouped_down_int4(
-    const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
-    const int32_t* __restrict__ sorted, const int32_t* __restrict__ blocks,
-    const int32_t* __restrict__ num_padded, const uint32_t* __restrict__ q,
-    const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zp, float* __restrict__ yhat,
-    int mk, int E, int H, int I, int g, int b, int nblk) {
-  constexpr int kSlab = 32 * kSpw;
-  constexpr int kRowB = kSlab * 2 + 16;
-  constexpr int kChunks = kSlab / 8;
-  constexpr int kLoads = 2 * kSpw;               // hi and lo planes
-  constexpr int kMaxGroups = 64;
-  constexpr int kDepth = ring_depth<kSpw>();
-  __shared__ __align__(16) unsigned char bs[2][2][kMaxTok * kRowB];
-  __shared__ uint16_t ssh[kTileRows * kMaxGroups / 2];
-  __shared__ uint8_t szz[kTileRows * kMaxGroups / 2];
-  __shared__ int cols[kMaxTok];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int n = lane & 15, lq = lane >> 4;
-  const int ngroups = H / kTileRows;
-  const int ntasks = nblk * ngroups;
-  const int npad = num_padded[0];
-  const int words = I >> 3, gpr = I / g;
-  const int nslab = I / kSlab;
-
-  for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-    const int blk = task / ngroups;
-    const int ng = task - blk * ngroups;
-    if (blk * b >= npad) continue;
-    const int e = blocks[blk];
-    if (e < 0 || e >= E) continue;
-
-    const size_t tile0 = static_cast<size_t>(e) * H + ng * kTileRows;
-    const size_t row0 = tile0 + wave * 16;
-    const uint32_t* qa = q + (row0 + n) * words + kSpw * lq;
-    uint32_t wa[kDepth][kSpw];
+    const int nact = __builtin_popcount(amask);
+    int act[kMaxSub];                    // sub-tile of each active index
+    {
+      int m = amask;
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d)
-      if (d < nslab) load_words<kSpw>(qa + d * 4 * kSpw, wa[d]);
-    for (int v = threadIdx.x; v < kTileRows * gpr; v += kThreads) {
-      ssh[v] = sc[tile0 * gpr + v];
-      szz[v] = zp[tile0 * gpr + v];
+      for (int u = 0; u < kMaxSub; ++u) {
+        act[u] = m ? __builtin_ctz(m) : 0;
+        m &= m - 1;
+      }
     }
-    const BlockView bv = stage_block(sorted, blk, b, mk, cols, n);   // includes a barrier
+    // Ring geometry: one slot per slab holds the 128 weight rows, then the
+    // activations of every (plane, active sub-tile, step), 1 KB each.
+    const int nbdma = nact * kPlanes * kSteps;                 // activation DMAs per slab
+    const int slot_bytes = kABytes + nbdma * 1024;
+    const int depth_fit = kRingBytes / slot_bytes;
+    const int depth = depth_fit < kMaxDepth ? depth_fit : kMaxDepth;   // >= 2 by construction
+    constexpr int kADma = kABytes / 1024;                       // weight DMAs per slab
+    // This wave's DMAs per slab: weight DMA i goes to wave i, activation DMA
+    // i to wave i % 8.
+    const int my_b = nbdma > wave ? (nbdma - wave + kGemmWaves - 1) / kGemmWaves : 0;
+    const int per_slab = my_b + (wave < kADma ? 1 : 0);
 
-    uint4 breg[kLoads];
-    auto load_b = [&](int s) {
+    // Everything before this point is a plain load the compiler waits for;
+    // from here on the only vector-memory operations are the LDS-DMA loads
+    // below (and the epilogue stores after the slab loop).
+    wait_vm<0>();
+
+    const size_t ebase = static_cast<size_t>(e) * p.rows_per_expert + static_cast<size_t>(ng) * p.tile_stride;
+    // Scales and zeros of the tile's two row sets, all groups (whole 1 KB
+    // DMAs: lanes past a region re-read its first chunk and land in the
+    // set's unused tail).
 #pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int idx = threadIdx.x + kThreads * (u >> 1);
-        const int col = idx / kChunks, ch = idx - col * kChunks;
-        const int r = cols[col];
-        const uint16_t* src = (u & 1) ? a_lo : a_hi;
-        breg[u] = r >= 0 ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * I + s * kSlab + ch * 8)
-                         : make_uint4(0, 0, 0, 0);
+    for (int set = 0; set < 2; ++set) {
+      const size_t r0 = ebase + static_cast<size_t>(set) * p.set_stride;
+      const int nsc = (kTileRows * gpr * 2) / 16, nzp = (kTileRows * gpr) / 16;
+      const unsigned char* gsc = reinterpret_cast<const unsigned char*>(p.sc + r0 * gpr);
+      const unsigned char* gzp = p.zp + r0 * gpr;
+      const int w0 = set * 4;
+      for (int m = wave - w0; m >= 0 && m < 4 && m * kWave < nsc; m += 4) {
+        const int c = m * kWave + lane;
+        dma16(gsc + 16 * (c < nsc ? c : 0), lds_addr(ssh + set * kScStride + m * 1024));
       }
-    };
-    auto store_b = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < kLoads; ++u) {
-        const int idx = threadIdx.x + kThreads * (u >> 1);
-        const int col = idx / kChunks, ch = idx - col * kChunks;
-        *reinterpret_cast<uint4*>(&bs[buf][u & 1][col * kRowB + ch * 16]) = breg[u];
+      for (int m = wave - w0; m >= 0 && m < 4 && m * kWave < nzp; m += 4) {
+        const int c = m * kWave + lane;
+        dma16(gzp + 16 * (c < nzp ? c : 0), lds_addr(szz + set * kZpStride + m * 1024));
       }
+    }
+
+    // Weight DMA of this wave (if any): rows kRowsPerDma * wave + l % kRowsPerDma
+    // of the tile, chunk l / kRowsPerDma of the slab.
+    const uint32_t* qa = nullptr;
+    if (wave < kADma) {
+      const int tr = kRowsPerDma * wave + lane % kRowsPerDma;     // tile-local row
+      const int ch = lane / kRowsPerDma;
+      const size_t grow = ebase + static_cast<size_t>(tr / kTileRows) * p.set_stride + tr % kTileRows;
+      qa = p.q + grow * words + 4 * ch;
+    }
+    // This wave's activation DMAs (at most two per slab: nbdma <= 16):
+    // DMA i = ((plane * nact + u) * kSteps + j) is issued by wave i % 8 and
+    // reads step j of this lane's column in active sub-tile u.
+    const uint16_t* bsrc[2] = {p.b0, p.b0};
+    int boff[2] = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = wave + kGemmWaves * t;
+      if (i >= nbdma) continue;
+      const int j = i % kSteps;
+      const int pu = i / kSteps;
+      const int pl = (kPlanes == 2 && pu >= nact) ? 1 : 0;
+      int m = amask;                      // the (pu - pl * nact)-th active sub-tile
+      for (int v = pu - pl * nact; v > 0; --v) m &= m - 1;
+      const int st = __builtin_ctz(m);
+      const uint16_t* base = pl ? p.b1 : p.b0;
+      bsrc[t] = base + static_cast<size_t>(brow[16 * st + n]) * p.K + 32 * j + 8 * lq;
+      boff[t] = kABytes + i * 1024;
+    }
+    // Ring slots are walked with running offsets, and the DMA sources with
+    // running pointers: no divisions in the slab loop.
+    const int ring_used = depth * slot_bytes;
+    const uint16_t* bnext0 = bsrc[0];
+    const uint16_t* bnext1 = bsrc[1];
+    const uint32_t* anext = qa;
+    auto issue_next = [&](int off) {
+      unsigned char* slot = ring + off;
+      if (my_b > 0) dma16(bnext0, lds_addr(slot + boff[0]));
+      if (my_b > 1) dma16(bnext1, lds_addr(slot + boff[1]));
+      if (wave < kADma) dma16(anext, lds_addr(slot + wave * 1024));
+      bnext0 += kSlabK;
+      bnext1 += kSlabK;
+      anext += kSlabK / 8;
     };
 
-    floatx4 acc[kMaxSub];
+    floatx4 acc[kMaxSub];            // per active index u (sub-tile act[u])
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) acc[st] = floatx4{0, 0, 0, 0};
+    for (int u = 0; u < kMaxSub; ++u) acc[u] = floatx4{0, 0, 0, 0};
 
-    load_b(0);
-    store_b(0);
-    __syncthreads();
-    const int la = wave * 16 + n;
-    for (int s0 = 0; s0 < nslab; s0 += kDepth) {
+    // This lane's weight row within the tile, and where its words sit in a slot.
+    const int arow = 64 * rs + rl + n;
+    const int a_off = (arow / kRowsPerDma) * 1024 + 16 * (arow % kRowsPerDma) + 4 * lq;
+    // Scale and zero addresses of this lane (group 0); the group index is
+    // added per partial.
+    const uint16_t* sp = reinterpret_cast<const uint16_t*>(ssh + rs * kScStride) + (rl + 4 * lq) * gpr;
+    const unsigned char* zpl = szz + rs * kZpStride + (rl + n) * gpr;
+    // Group of the first partial of a slab: slab s covers groups s * gps ..
+    // (g below the slab) or group s / spg (g a multiple of the slab).
+    const int gps = p.g < kSlabK ? kSlabK / p.g : 1;
+    const int spg = p.g < kSlabK ? 1 : p.g / kSlabK;
+
+    int wr = 0;
+    for (int s = 0; s < depth - 1 && s < nslab; ++s) {
+      issue_next(wr);
+      wr += slot_bytes;
+    }
+    const int n_steady = (depth - 2) * per_slab;
+    int rd = 0, grp0 = 0, gcount = 0;
+    for (int s = 0; s < nslab; ++s) {
+      const bool more = s + depth - 1 < nslab;
+      wait_vm_le(more ? n_steady : (nslab - 1 - s) * per_slab);
+      lds_barrier();
+      if (more) {
+        issue_next(wr);
+        wr += slot_bytes;
+        if (wr == ring_used) wr = 0;
+      }
+      const unsigned char* slot = ring + rd;
+      rd += slot_bytes;
+      if (rd == ring_used) rd = 0;
+      // Step j, lane group q: word 4j + q of the row = word q of chunk j.
+      uint32_t aw[kSteps];
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int s = s0 + d;
-        if (s >= nslab) break;
-        const int cur = s & 1;
-        const int grp = (s * kSlab) / g;
-        const float za = static_cast<float>(szz[la * gpr + grp]);
-        bf16x8 A[kSpw];
+      for (int j = 0; j < kSteps; ++j)
+        aw[j] = *reinterpret_cast<const uint32_t*>(slot + a_off + 16 * kRowsPerDma * j);
 #pragma unroll
-        for (int j = 0; j < kSpw; ++j) A[j] = dequant8_exact(wa[d][j], za);
-        if (s + 1 < nslab) load_b(s + 1);
-        if (s + kDepth < nslab) load_words<kSpw>(qa + (s + kDepth) * 4 * kSpw, wa[d]);
+      for (int f = 0; f < kSteps / kFlush; ++f) {
+        const int grp = grp0 + f;
+        const bf16x8 Z = neg_zero_pairs(zpl[grp]);
         float cs[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(ssh[(wave * 16 + 4 * lq + i) * gpr + grp]);
+        for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(sp[i * gpr + grp]);
+        bf16x8 A[kFlush];
 #pragma unroll
-        for (int st = 0; st < kMaxSub; ++st) {
-          if (!bv.act[st]) continue;
-          const int boff = (16 * st + n) * kRowB + 16 * kSpw * lq;
-          floatx4 dd = {0, 0, 0, 0};
+        for (int jj = 0; jj < kFlush; ++jj) A[jj] = bias_pairs(aw[kFlush * f + jj], nib_mask);
 #pragma unroll
-          for (int j = 0; j < kSpw; ++j) {
-            const bf16x8 Bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bs[cur][0][boff + 16 * j]));
-            const bf16x8 Bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bs[cur][1][boff + 16 * j]));
-            dd = mfma_bf16(A[j], Bh, dd);
-            dd = mfma_bf16(A[j], Bl, dd);
+        for (int u = 0; u < kMaxSub; ++u) {
+          if (u >= nact) break;
+          // One chain per active sub-tile: the bias product and the
+          // zero-point product accumulate into the same partial.
+          floatx4 d = {0, 0, 0, 0};
+#pragma unroll
+          for (int jj = 0; jj < kFlush; ++jj) {
+            const int j = kFlush * f + jj;
+#pragma unroll
+            for (int pl = 0; pl < kPlanes; ++pl) {
+              const bf16x8 B = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const uint4*>(slot + kABytes + (((pl * nact + u) * kSteps + j) * 1024) + 16 * lane));
+              d = mfma_bf16(A[jj], B, d);
+              d = mfma_bf16(Z, B, d);
+            }
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[st][i] = fmaf(cs[i], dd[i], acc[st][i]);
+          for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(cs[i], d[i], acc[u][i]);
         }
-        if (s + 1 < nslab) store_b(cur ^ 1);
-        __syncthreads();
+      }
+      if (++gcount == spg) {
+        gcount = 0;
+        grp0 += gps;
       }
     }
+
+    // Epilogue: every valid column's rows are written once.
+    if constexpr (kGateUp) {
+      // The up waves hand their sums to the gate waves through the ring.
+      lds_barrier();
+      float* xch = reinterpret_cast<float*>(ring);
+      if (rs == 1) {
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) {
-      const int r = bv.rid[st];
-      if (r < 0) continue;
-      *reinterpret_cast<float4*>(yhat + static_cast<size_t>(r) * H + ng * kTileRows + wave * 16 + 4 * lq) =
-          make_float4(acc[st][0], acc[st][1], acc[st][2], acc[st][3]);
+        for (int u = 0; u < kMaxSub; ++u)
+          *reinterpret_cast<floatx4*>(xch + (((wave & 3) * kMaxSub + u) * kWave + lane) * 4) = acc[u];
+      }
+      lds_barrier();
+      if (rs == 0) {
+#pragma unroll
+        for (int u = 0; u < kMaxSub; ++u) {
+          if (u >= nact) break;
+          const int r = cols[16 * act[u] + n];
+          if (r < 0) continue;
+          const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kMaxSub + u) * kWave + lane) * 4);
+          uint32_t hi2[2], lo2[2];
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float v0 = silu_mul(acc[u][i], up[i]);
+            const float v1 = silu_mul(acc[u][i + 1], up[i + 1]);
+            const bf16x2 h = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
+            const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+            const bf16x2 l = {static_cast<__bf16>(v0 - bf16_lo(hb)), static_cast<__bf16>(v1 - bf16_hi(hb))};
+            hi2[i / 2] = hb;
+            lo2[i / 2] = __builtin_bit_cast(uint32_t, l);
+          }
+          const size_t off = static_cast<size_t>(r) * p.out_rows + ng * p.tile_stride + rl + 4 * lq;
+          *reinterpret_cast<uint2*>(p.a_hi + off) = make_uint2(hi2[0], hi2[1]);
+          *reinterpret_cast<uint2*>(p.a_lo + off) = make_uint2(lo2[0], lo2[1]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kMaxSub; ++u) {
+        if (u >= nact) break;
+        const int r = cols[16 * act[u] + n];
+        if (r < 0) continue;
+        const size_t off = static_cast<size_t>(r) * p.out_rows + ng * p.tile_stride + 64 * rs + rl + 4 * lq;
+        *reinterpret_cast<float4*>(p.yhat + off) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+      }
     }
+    __syncthreads();   // cols, brow and the ring are reused by the next task
   }
 }
 
@@ -431,80 +452,98 @@ int grid_for(int work_groups, int max_workgroups) {
   return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : work_groups;
 }
 
-int slab_words(int K, int g, int max_spw) {
-  // Largest of 4, 2, 1 words per lane (slabs of 128, 64, 32 elements), at
-  // most max_spw, such that a slab stays inside one group and K is a whole
-  // number of slabs.
-  for (int spw = max_spw; spw >= 1; spw >>= 1) {
-    const int slab = 32 * spw;
-    if (g % slab == 0 && K % slab == 0) return spw;
-  }
-  return 0;
+// Steps per scaled partial: g / 32 for g below the slab, else a whole slab
+// (g a multiple of the slab).
+int flush_steps(int g, int steps) { return g >= 32 * steps ? steps : g / 32; }
+
+bool group_ok(int K, int g, int slab) {
+  if (g < 32 || (g % 32) != 0 || (K % g) != 0 || K / g > kMaxGpr) return false;
+  return g < slab ? (slab % g) == 0 : (g % slab) == 0;
 }
 
-// The down kernel stages two planes, so its slab is at most 64 elements to
-// keep the double-buffered LDS tile small.
-#ifndef MOE_GATE_UP_MAX_SPW
-#define MOE_GATE_UP_MAX_SPW 4
-#endif
-constexpr int kGateUpMaxSpw = MOE_GATE_UP_MAX_SPW;
-constexpr int kDownMaxSpw = 2;
+template <bool kGateUp, int kPlanes, int kSteps>
+hipError_t launch_gemm(const GemmParams& gp, int wgs, hipStream_t stream) {
+  switch (flush_steps(gp.g, kSteps)) {
+    case 1:
+      hipLaunchKernelGGL((grouped_gemm_int4<kGateUp, kPlanes, kSteps, 1>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      break;
+    case 2:
+      hipLaunchKernelGGL((grouped_gemm_int4<kGateUp, kPlanes, kSteps, 2>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      break;
+    default:
+      hipLaunchKernelGGL((grouped_gemm_int4<kGateUp, kPlanes, kSteps, kSteps>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      break;
+  }
+  return hipGetLastError();
+}
+
+constexpr int kGateUpSteps = 4;   // 128-element slabs
+constexpr int kDownSteps = 2;     // 64-element slabs (two planes of activations)
 
 }  // namespace
 
 bool grouped_shape_ok(int H, int I, int b, int g13, int g2) {
-  // The scale/zero tiles of a workgroup live in LDS: at most 16 groups per
-  // row for W13 and 32 for W2.
-  return b >= 1 && b <= kMaxTok && (I % kTileRows) == 0 && (H % kTileRows) == 0 &&
-         slab_words(H, g13, kGateUpMaxSpw) > 0 && slab_words(I, g2, kDownMaxSpw) > 0 &&
-         H / g13 <= 16 && I / g2 <= 32;
+  // Whole slabs and whole tiles in both GEMMs (gate/up: 64 neurons; down:
+  // 128 rows); the tile's scales and zeros (at most 32 groups per row) are
+  // staged in LDS.
+  return b >= 1 && b <= kMaxTok && (H % 128) == 0 && (I % 64) == 0 && (H % (32 * kGateUpSteps)) == 0 &&
+         (I % (32 * kDownSteps)) == 0 && group_ok(H, g13, 32 * kGateUpSteps) &&
+         group_ok(I, g2, 32 * kDownSteps);
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
-  const int ntasks = p.nblk * (p.I / kTileRows);
-  const int wgs = grid_for(ntasks, p.max_workgroups);
-  const auto* q = static_cast<const uint32_t*>(p.w13.q);
-  const auto* s = static_cast<const uint16_t*>(p.w13.scale);
-  const int mk = p.M * p.k;
-  switch (slab_words(p.H, p.w13.group, kGateUpMaxSpw)) {
-    case 4:
-      hipLaunchKernelGGL(grouped_gate_up_int4<4>, dim3(wgs), dim3(kThreads), 0, stream, p.x, p.sorted,
-                         p.blocks, p.num_padded, q, s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H,
-                         p.I, p.w13.group, p.b, p.nblk);
-      break;
-    case 2:
-      hipLaunchKernelGGL(grouped_gate_up_int4<2>, dim3(wgs), dim3(kThreads), 0, stream, p.x, p.sorted,
-                         p.blocks, p.num_padded, q, s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H,
-                         p.I, p.w13.group, p.b, p.nblk);
-      break;
-    default:
-      hipLaunchKernelGGL(grouped_gate_up_int4<1>, dim3(wgs), dim3(kThreads), 0, stream, p.x, p.sorted,
-                         p.blocks, p.num_padded, q, s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H,
-                         p.I, p.w13.group, p.b, p.nblk);
-      break;
-  }
-  return hipGetLastError();
+  GemmParams gp{};
+  gp.b0 = p.x;
+  gp.b1 = nullptr;
+  gp.sorted = p.sorted;
+  gp.blocks = p.blocks;
+  gp.num_padded = p.num_padded;
+  gp.q = static_cast<const uint32_t*>(p.w13.q);
+  gp.sc = static_cast<const uint16_t*>(p.w13.scale);
+  gp.zp = p.w13.zero;
+  gp.a_hi = p.a_hi;
+  gp.a_lo = p.a_lo;
+  gp.mk = p.M * p.k;
+  gp.k = p.k;
+  gp.E = p.E;
+  gp.b = p.b;
+  gp.nblk = p.nblk;
+  gp.ntile = p.I / kTileRows;
+  gp.rows_per_expert = 2 * p.I;
+  gp.set_stride = p.I;
+  gp.tile_stride = kTileRows;
+  gp.out_rows = p.I;
+  gp.K = p.H;
+  gp.g = p.w13.group;
+  const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
+  return launch_gemm<true, 1, kGateUpSteps>(gp, wgs, stream);
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
-  const int ntasks = p.nblk * (p.H / kTileRows);
-  const int wgs = grid_for(ntasks, p.max_workgroups);
-  const auto* q = static_cast<const uint32_t*>(p.w2.q);
-  const auto* s = static_cast<const uint16_t*>(p.w2.scale);
-  const int mk = p.M * p.k;
-  switch (slab_words(p.I, p.w2.group, kDownMaxSpw)) {
-    case 2:
-      hipLaunchKernelGGL(grouped_down_int4<2>, dim3(wgs), dim3(kThreads), 0, stream, p.a_hi, p.a_lo,
-                         p.sorted, p.blocks, p.num_padded, q, s, p.w2.zero, p.yhat, mk, p.E, p.H,
-                         p.I, p.w2.group, p.b, p.nblk);
-      break;
-    default:
-      hipLaunchKernelGGL(grouped_down_int4<1>, dim3(wgs), dim3(kThreads), 0, stream, p.a_hi, p.a_lo,
-                         p.sorted, p.blocks, p.num_padded, q, s, p.w2.zero, p.yhat, mk, p.E, p.H,
-                         p.I, p.w2.group, p.b, p.nblk);
-      break;
-  }
-  return hipGetLastError();
+  GemmParams gp{};
+  gp.b0 = p.a_hi;
+  gp.b1 = p.a_lo;
+  gp.sorted = p.sorted;
+  gp.blocks = p.blocks;
+  gp.num_padded = p.num_padded;
+  gp.q = static_cast<const uint32_t*>(p.w2.q);
+  gp.sc = static_cast<const uint16_t*>(p.w2.scale);
+  gp.zp = p.w2.zero;
+  gp.yhat = p.yhat;
+  gp.mk = p.M * p.k;
+  gp.k = p.k;
+  gp.E = p.E;
+  gp.b = p.b;
+  gp.nblk = p.nblk;
+  gp.ntile = p.H / (2 * kTileRows);
+  gp.rows_per_expert = p.H;
+  gp.set_stride = kTileRows;
+  gp.tile_stride = 2 * kTileRows;
+  gp.out_rows = p.H;
+  gp.K = p.I;
+  gp.g = p.w2.group;
+  const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
+  return launch_gemm<false, 2, kDownSteps>(gp, wgs, stream);
 }
 
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream) {

@@ -65,6 +65,8 @@ RAGGED = [
     dict(M=3, H=192, I=64, E=8, k=3, b=8, g=32),
     dict(M=2, H=320, I=448, E=16, k=5, b=8, g=64),
     dict(M=2, H=256, I=1536, E=16, k=12, b=8, g=128),
+    # A group spanning two 128-element slabs.
+    dict(M=6, H=512, I=256, E=8, k=2, b=16, g=256),
 ]
 
 
