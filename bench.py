@@ -49,6 +49,12 @@ def parse():
     return p.parse_args()
 
 
+def _clone_projection(p):
+    import mixture_experts_ffn_align_amd as moe
+    return moe.DeviceProjection(p.fmt, p.group, p.q.clone(), p.scale.clone(),
+                                None if p.zero is None else p.zero.clone())
+
+
 class Rotation:
     """Device inputs for one workload: layer copies and routings."""
 
@@ -64,10 +70,8 @@ class Rotation:
         base2 = moe.DeviceProjection.from_host(w2, "cuda")
         self.layers = []
         for i in range(n_layers):
-            p13 = base13 if i == 0 else moe.DeviceProjection(
-                base13.fmt, base13.group, base13.q.clone(), base13.scale.clone(), base13.zero.clone())
-            p2 = base2 if i == 0 else moe.DeviceProjection(
-                base2.fmt, base2.group, base2.q.clone(), base2.scale.clone(), base2.zero.clone())
+            p13 = base13 if i == 0 else _clone_projection(base13)
+            p2 = base2 if i == 0 else _clone_projection(base2)
             self.layers.append(moe.MoeLayer(p13, p2, cfg.E, cfg.H, cfg.I, cfg.k, cfg.b))
         self.inputs = []
         self.host_inputs = []

@@ -52,7 +52,7 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if ((d->H % 32) != 0 || (d->I % 32) != 0) return MOE_ERR_INVALID_ARG;
   if ((d->H % d->w13.group) != 0 || (d->I % d->w2.group) != 0) return MOE_ERR_INVALID_ARG;
   if ((d->w13.group % 32) != 0 || (d->w2.group % 32) != 0) return MOE_ERR_INVALID_ARG;
-  if (d->w13.fmt == MOE_W_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (d->w13.fmt == MOE_W_MXFP8 && (d->w13.group != 32 || d->w2.group != 32)) return MOE_ERR_INVALID_ARG;
   if (d->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   const int64_t mk = int64_t(d->M) * d->k;
   if (mk > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
@@ -62,14 +62,14 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (need_align_buffers) path = MOE_PATH_GROUPED;
   L->path = path;
   if (path == MOE_PATH_DECODE) {
-    if (!moe::decode_shape_ok(d->H, d->I, d->k, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
+    if (!moe::decode_shape_ok(d->w13.fmt, d->H, d->I, d->k, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
     L->off_a = 0;
     L->off_a_lo = round256(size_t(mk) * d->I * sizeof(uint16_t));
     L->total = L->off_a_lo + round256(size_t(mk) * d->I * sizeof(uint16_t));
     if (L->total == 0) L->total = 256;
     return MOE_OK;
   }
-  if (!moe::grouped_shape_ok(d->H, d->I, d->b, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
+  if (!moe::grouped_shape_ok(d->w13.fmt, d->H, d->I, d->b, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
   L->cap = capacity_of(d->M, d->k, d->E, d->b);
   size_t o = 0;
   L->off_sorted = o; o += round256(L->cap * sizeof(int32_t));

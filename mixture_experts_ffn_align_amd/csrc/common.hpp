@@ -18,7 +18,26 @@ __device__ __forceinline__ uint4 load_stream16(const uint32_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 constexpr int kWave = 64;
+
+// Two OCP E4M3 codes (the low or the high 16 bits of w, low byte first) -> a
+// bf16 pair in the same order. Exact: every E4M3 value is a bf16 value.
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+// E8M0 block scale byte -> 2^(e - 127) in fp32 (e = 0 is the subnormal
+// 2^-127, e = 255 is NaN).
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+  const uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23);
+  return __uint_as_float(bits);
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));

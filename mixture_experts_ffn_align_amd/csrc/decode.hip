@@ -60,18 +60,65 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-__global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
+// One 32-element chunk of a weight row dotted with 16 bf16 activation pairs
+// (xw). int4: 16 bytes, bf16 (128 + q) pairs, the caller removes the bias
+// and zero point; MXFP8: 32 bytes of E4M3 codes, converted exactly to bf16
+// pairs, the caller applies the block's power-of-two scale.
+template <int kFmt>
+struct ChunkRow {
+  static constexpr int kVecs = kFmt == MOE_W_MXFP8 ? 2 : 1;   // 16-byte loads per chunk
+  uint4 v[kVecs];
+};
+
+template <int kFmt>
+__device__ __forceinline__ void load_chunk(const unsigned char* row, int c, ChunkRow<kFmt>& w) {
+  const uint4* p = reinterpret_cast<const uint4*>(row) + c * ChunkRow<kFmt>::kVecs;
+#pragma unroll
+  for (int i = 0; i < ChunkRow<kFmt>::kVecs; ++i) w.v[i] = load_stream16(p + i);
+}
+
+template <int kFmt>
+__device__ __forceinline__ float dot_chunk(const ChunkRow<kFmt>& w, const uint32_t (&xw)[16], uint32_t nib_mask,
+                                           float d) {
+  if constexpr (kFmt == MOE_W_MXFP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w4[4] = {w.v[i].x, w.v[i].y, w.v[i].z, w.v[i].w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        d = dot2_bf16(fp8x2_to_bf16x2<false>(w4[v]), xw[8 * i + 2 * v], d);
+        d = dot2_bf16(fp8x2_to_bf16x2<true>(w4[v]), xw[8 * i + 2 * v + 1], d);
+      }
+    }
+  } else {
+    const uint32_t w4[4] = {w.v[0].x, w.v[0].y, w.v[0].z, w.v[0].w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t p[4];
+      unpack8_bias128_m(w4[v], nib_mask, p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d = dot2_bf16(p[i], xw[4 * v + i], d);
+    }
+  }
+  return d;
+}
+
+template <int kFmt>
+__global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-    const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
+    const unsigned char* __restrict__ q, const unsigned char* __restrict__ sc,
     const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
     int mk, int k, int E, int H, int I, int g_shift) {
+  constexpr bool kMx = kFmt == MOE_W_MXFP8;
   const int lane = threadIdx.x & (kWave - 1);
   // Task indices are wave-uniform: keep them (and the row addresses) scalar.
   const int wave_id = uniform(blockIdx.x * kGateUpWaves + threadIdx.x / kWave);
   const int nwaves = gridDim.x * kGateUpWaves;
   const int tasks_per_route = I / kNpw;
   const int ntasks = mk * tasks_per_route;
-  const int nch = H >> 5, words = H >> 3, gpr = H >> g_shift;
+  const int nch = H >> 5, gpr = H >> g_shift;
+  const int row_bytes = kMx ? H : H / 2;
+  const int sc_bytes = kMx ? 1 : 2;                // E8M0 byte or fp16 per group
   const uint32_t nib_mask = in_vgpr(0x000F000Fu);
 
   for (int task = wave_id; task < ntasks; task += nwaves) {
@@ -87,15 +134,15 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     }
     const int t = r / k;
     const size_t row0 = static_cast<size_t>(e) * (2 * I) + i0;  // first gate row
-    const uint32_t* qrow[2 * kNpw];
-    const uint16_t* srow[2 * kNpw];
+    const unsigned char* qrow[2 * kNpw];
+    const unsigned char* srow[2 * kNpw];
     const uint8_t* zrow[2 * kNpw];
 #pragma unroll
     for (int j = 0; j < 2 * kNpw; ++j) {
       const size_t row = row0 + (j < kNpw ? j : I + j - kNpw);
-      qrow[j] = q + row * words;
-      srow[j] = sc + row * gpr;
-      zrow[j] = zp + row * gpr;
+      qrow[j] = q + row * row_bytes;
+      srow[j] = sc + row * gpr * sc_bytes;
+      zrow[j] = kMx ? nullptr : zp + row * gpr;
     }
     float acc[2 * kNpw];
 #pragma unroll
@@ -103,45 +150,45 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
     const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
     for (int c = lane; c < nch; c += kWave) {
       // Issue the weight loads first so they are all in flight together.
-      uint4 wv[2 * kNpw];
-      float s[2 * kNpw], zb[2 * kNpw];
+      ChunkRow<kFmt> wv[2 * kNpw];
       const int grp = (c << 5) >> g_shift;
 #pragma unroll
-      for (int j = 0; j < 2 * kNpw; ++j) wv[j] = load_stream16(qrow[j] + 4 * c);
+      for (int j = 0; j < 2 * kNpw; ++j) load_chunk<kFmt>(qrow[j], c, wv[j]);
       uint32_t sv[2 * kNpw], zv[2 * kNpw];
 #pragma unroll
-      for (int j = 0; j < 2 * kNpw; ++j) { sv[j] = srow[j][grp]; zv[j] = zrow[j][grp]; }
+      for (int j = 0; j < 2 * kNpw; ++j) {
+        if constexpr (kMx) {
+          sv[j] = srow[j][grp];
+        } else {
+          sv[j] = reinterpret_cast<const uint16_t*>(srow[j])[grp];
+          zv[j] = zrow[j][grp];
+        }
+      }
       uint4 xv[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) xv[v] = xrow[c * 4 + v];
       // Keep every load above this point: the scheduler would otherwise sink
       // some of them below the first use of the others and add a round trip.
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 2 * kNpw; ++j) {
-        s[j] = half_bits_to_float(static_cast<uint16_t>(sv[j]));
-        zb[j] = 128.0f + static_cast<float>(zv[j]);
-      }
       uint32_t xw[16];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         xw[4 * v] = xv[v].x; xw[4 * v + 1] = xv[v].y; xw[4 * v + 2] = xv[v].z; xw[4 * v + 3] = xv[v].w;
       }
-      float sx = 0.0f;
+      if constexpr (kMx) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sx = dot2_bf16(xw[v], 0x3F803F80u, sx);  // (1.0, 1.0)
+        for (int j = 0; j < 2 * kNpw; ++j)
+          acc[j] = fmaf(e8m0_to_float(sv[j]), dot_chunk<kFmt>(wv[j], xw, nib_mask, 0.0f), acc[j]);
+      } else {
+        float sx = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 2 * kNpw; ++j) {
-        const uint32_t w4[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-        float d = 0.0f;
+        for (int v = 0; v < 16; ++v) sx = dot2_bf16(xw[v], 0x3F803F80u, sx);  // (1.0, 1.0)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          uint32_t p[4];
-          unpack8_bias128_m(w4[v], nib_mask, p);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d = dot2_bf16(p[i], xw[4 * v + i], d);
+        for (int j = 0; j < 2 * kNpw; ++j) {
+          const float s = half_bits_to_float(static_cast<uint16_t>(sv[j]));
+          const float zb = 128.0f + static_cast<float>(zv[j]);
+          acc[j] = fmaf(s, fmaf(-zb, sx, dot_chunk<kFmt>(wv[j], xw, nib_mask, 0.0f)), acc[j]);
         }
-        acc[j] = fmaf(s[j], fmaf(-zb[j], sx, d), acc[j]);
       }
     }
 #pragma unroll
@@ -164,13 +211,14 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up_int4(
 // kSpan: lanes per slot, pow2(I/32) capped at 64; kCh: 32-element chunks of
 // a down row per lane (1, or 2 when I/32 > 64). Routes j = wave, wave + 8, ...
 // are taken in turn.
-template <int kCh, int kSpan>
-__global__ __launch_bounds__(kDownThreads) void decode_down_int4(
+template <int kFmt, int kCh, int kSpan>
+__global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
-    const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
+    const unsigned char* __restrict__ q, const unsigned char* __restrict__ sc,
     const uint8_t* __restrict__ zp, float* __restrict__ y, int M, int k, int E, int H, int I,
     int g_shift) {
+  constexpr bool kMx = kFmt == MOE_W_MXFP8;
   constexpr int kSlots = kWave / kSpan;
   constexpr int kRps = (kDownRows + kSlots - 1) / kSlots;  // rows per lane
   __shared__ float part[kDownWaves][kDownRows];
@@ -178,7 +226,9 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
   const int wave = uniform(threadIdx.x / kWave);
   const int tiles_per_tok = H / kDownRows;
   const int ntiles = M * tiles_per_tok;
-  const int nch = I >> 5, words = I >> 3, gpr = I >> g_shift;
+  const int nch = I >> 5, gpr = I >> g_shift;
+  const int row_bytes = kMx ? I : I / 2;
+  const int sc_bytes = kMx ? 1 : 2;
   const int span = kSpan, slots = kSlots;
   const int slot = lane / kSpan;
   const int c0 = lane - slot * kSpan;
@@ -230,22 +280,26 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
       const int e_raw = uniform(load_expert(ids, static_cast<int>(r), E));
       const int e = e_raw < 0 ? 0 : e_raw;
       const float wr = e_raw < 0 ? 0.0f : topk_w[r];
-      const uint32_t* qt = q + (static_cast<size_t>(e) * H + h0) * words;
+      const unsigned char* qt = q + (static_cast<size_t>(e) * H + h0) * row_bytes;
       const size_t gt = (static_cast<size_t>(e) * H + h0) * gpr;
-      uint4 wv[kCh][kRps];
+      ChunkRow<kFmt> wv[kCh][kRps];
       uint32_t sv[kCh][kRps], zv[kCh][kRps];
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
 #pragma unroll
-        for (int i = 0; i < kRps; ++i) wv[cc][i] = load_stream16(qt + mrow[i] * words + 4 * cl[cc]);
+        for (int i = 0; i < kRps; ++i) load_chunk<kFmt>(qt + mrow[i] * row_bytes, cl[cc], wv[cc][i]);
       }
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
         const int grp = (cl[cc] << 5) >> g_shift;
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
-          sv[cc][i] = sc[gt + mrow[i] * gpr + grp];
-          zv[cc][i] = zp[gt + mrow[i] * gpr + grp];
+          if constexpr (kMx) {
+            sv[cc][i] = sc[gt + mrow[i] * gpr + grp];
+          } else {
+            sv[cc][i] = reinterpret_cast<const uint16_t*>(sc)[gt + mrow[i] * gpr + grp];
+            zv[cc][i] = zp[gt + mrow[i] * gpr + grp];
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -259,35 +313,29 @@ __global__ __launch_bounds__(kDownThreads) void decode_down_int4(
                                  lv[cc][1].x, lv[cc][1].y, lv[cc][1].z, lv[cc][1].w,
                                  lv[cc][2].x, lv[cc][2].y, lv[cc][2].z, lv[cc][2].w,
                                  lv[cc][3].x, lv[cc][3].y, lv[cc][3].z, lv[cc][3].w};
-        // Sum of the chunk's activations in four independent chains.
-        float sa4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // Sum of the chunk's activations in four independent chains (int4:
+        // the bias and zero-point term).
+        float sa = 0.0f;
+        if constexpr (!kMx) {
+          float sa4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          sa4[v & 3] = dot2_bf16(lw[v], 0x3F803F80u, dot2_bf16(hw[v], 0x3F803F80u, sa4[v & 3]));
-        const float sa = (sa4[0] + sa4[1]) + (sa4[2] + sa4[3]);
-        // Per row, the hi and lo planes are separate chains.
-        float dh[kRps], dl[kRps];
-#pragma unroll
-        for (int i = 0; i < kRps; ++i) { dh[i] = 0.0f; dl[i] = 0.0f; }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-#pragma unroll
-          for (int i = 0; i < kRps; ++i) {
-            const uint32_t w = v == 0 ? wv[cc][i].x : v == 1 ? wv[cc][i].y : v == 2 ? wv[cc][i].z : wv[cc][i].w;
-            uint32_t p[4];
-            unpack8_bias128_m(w, nib_mask, p);
-#pragma unroll
-            for (int e8 = 0; e8 < 4; ++e8) {
-              dh[i] = dot2_bf16(p[e8], hw[4 * v + e8], dh[i]);
-              dl[i] = dot2_bf16(p[e8], lw[4 * v + e8], dl[i]);
-            }
-          }
+          for (int v = 0; v < 16; ++v)
+            sa4[v & 3] = dot2_bf16(lw[v], 0x3F803F80u, dot2_bf16(hw[v], 0x3F803F80u, sa4[v & 3]));
+          sa = (sa4[0] + sa4[1]) + (sa4[2] + sa4[3]);
         }
+        // Per row, the hi and lo planes are separate chains.
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
-          const float s = cvalid[cc] * half_bits_to_float(static_cast<uint16_t>(sv[cc][i]));
-          const float zb = 128.0f + static_cast<float>(zv[cc][i]);
-          acc[i] = fmaf(wr * s, fmaf(-zb, sa, dh[i] + dl[i]), acc[i]);
+          const float dh = dot_chunk<kFmt>(wv[cc][i], hw, nib_mask, 0.0f);
+          const float dl = dot_chunk<kFmt>(wv[cc][i], lw, nib_mask, 0.0f);
+          if constexpr (kMx) {
+            const float s = cvalid[cc] * e8m0_to_float(sv[cc][i]);
+            acc[i] = fmaf(wr * s, dh + dl, acc[i]);
+          } else {
+            const float s = cvalid[cc] * half_bits_to_float(static_cast<uint16_t>(sv[cc][i]));
+            const float zb = 128.0f + static_cast<float>(zv[cc][i]);
+            acc[i] = fmaf(wr * s, fmaf(-zb, sa, dh + dl), acc[i]);
+          }
         }
       }
     }
@@ -344,17 +392,32 @@ int log2_of(int g) {
   return s;
 }
 
-template <int kCh, int kSpan>
+template <int kFmt, int kCh, int kSpan>
 void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_down_int4<kCh, kSpan>), dim3(wgs), dim3(kDownThreads), 0, stream,
-                     p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const uint32_t*>(p.w2.q),
-                     static_cast<const uint16_t*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E, p.H,
-                     p.I, log2_of(p.w2.group));
+  hipLaunchKernelGGL((decode_down<kFmt, kCh, kSpan>), dim3(wgs), dim3(kDownThreads), 0, stream,
+                     p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const unsigned char*>(p.w2.q),
+                     static_cast<const unsigned char*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E,
+                     p.H, p.I, log2_of(p.w2.group));
+}
+
+template <int kFmt>
+void launch_down_fmt(const DecodeArgs& p, int wgs, hipStream_t stream) {
+  const int nch = p.I >> 5;
+  if (nch > 32) {
+    if (nch > kWave) launch_down<kFmt, 2, 64>(p, wgs, stream);
+    else launch_down<kFmt, 1, 64>(p, wgs, stream);
+  } else if (nch > 16) launch_down<kFmt, 1, 32>(p, wgs, stream);
+  else if (nch > 8) launch_down<kFmt, 1, 16>(p, wgs, stream);
+  else if (nch > 4) launch_down<kFmt, 1, 8>(p, wgs, stream);
+  else if (nch > 2) launch_down<kFmt, 1, 4>(p, wgs, stream);
+  else if (nch > 1) launch_down<kFmt, 1, 2>(p, wgs, stream);
+  else launch_down<kFmt, 1, 1>(p, wgs, stream);
 }
 
 }  // namespace
 
-bool decode_shape_ok(int H, int I, int k, int g13, int g2) {
+bool decode_shape_ok(int fmt, int H, int I, int k, int g13, int g2) {
+  if (fmt == MOE_W_MXFP8 && (g13 != 32 || g2 != 32)) return false;
   // Two 32-element chunks of a down row per lane at most (I <= 4096), at most
   // two routes per down wave (k <= 16), and power-of-two groups (the kernels
   // divide by shifting).
@@ -367,24 +430,21 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const int mk = p.M * p.k;
   const int waves = mk * (p.I / kNpw);
   const int wgs = grid_for((waves + kGateUpWaves - 1) / kGateUpWaves, p.max_workgroups);
-  hipLaunchKernelGGL(decode_gate_up_int4, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids,
-                     static_cast<const uint32_t*>(p.w13.q), static_cast<const uint16_t*>(p.w13.scale),
-                     p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H, p.I, log2_of(p.w13.group));
+  const auto* q = static_cast<const unsigned char*>(p.w13.q);
+  const auto* s = static_cast<const unsigned char*>(p.w13.scale);
+  if (p.w13.fmt == MOE_W_MXFP8)
+    hipLaunchKernelGGL(decode_gate_up<MOE_W_MXFP8>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q, s,
+                       p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H, p.I, log2_of(p.w13.group));
+  else
+    hipLaunchKernelGGL(decode_gate_up<MOE_W_INT4_AWQ>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q,
+                       s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H, p.I, log2_of(p.w13.group));
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream) {
   const int wgs = grid_for(p.M * (p.H / kDownRows), p.max_workgroups);
-  const int nch = p.I >> 5;
-  if (nch > 32) {
-    if (nch > kWave) launch_down<2, 64>(p, wgs, stream);
-    else launch_down<1, 64>(p, wgs, stream);
-  } else if (nch > 16) launch_down<1, 32>(p, wgs, stream);
-  else if (nch > 8) launch_down<1, 16>(p, wgs, stream);
-  else if (nch > 4) launch_down<1, 8>(p, wgs, stream);
-  else if (nch > 2) launch_down<1, 4>(p, wgs, stream);
-  else if (nch > 1) launch_down<1, 2>(p, wgs, stream);
-  else launch_down<1, 1>(p, wgs, stream);
+  if (p.w2.fmt == MOE_W_MXFP8) launch_down_fmt<MOE_W_MXFP8>(p, wgs, stream);
+  else launch_down_fmt<MOE_W_INT4_AWQ>(p, wgs, stream);
   return hipGetLastError();
 }
 

@@ -128,8 +128,8 @@ struct GemmParams {
   const int32_t* sorted;
   const int32_t* blocks;
   const int32_t* num_padded;
-  const uint32_t* q;             // [E][rows_per_expert][K/8]
-  const uint16_t* sc;            // [E][rows_per_expert][K/g]
+  const unsigned char* q;        // int4: u32 [E][rows][K/8]; MXFP8: E4M3 [E][rows][K]
+  const unsigned char* sc;       // int4: fp16 [E][rows][K/g]; MXFP8: E8M0 [E][rows][K/32]
   const uint8_t* zp;
   uint16_t* a_hi;                // gate/up output planes [Mk][I]
   uint16_t* a_lo;
@@ -155,15 +155,18 @@ constexpr int kMaxDepth = 8;
 // kGateUp: epilogue silu(gate) * up (else yhat rows). kPlanes: B planes (1: x;
 // 2: the hi and lo planes). kSteps: 32-element MFMA steps per slab (4 or 2).
 // kFlush: steps per scaled partial (g / 32, at most kSteps).
-template <bool kGateUp, int kPlanes, int kSteps, int kFlush>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmParams p) {
+template <int kFmt, bool kGateUp, int kPlanes, int kSteps, int kFlush>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p) {
+  constexpr bool kMx = kFmt == MOE_W_MXFP8;
   constexpr int kSlabK = 32 * kSteps;                  // reduction elements per slab
-  constexpr int kRowBytes = kSlabK / 2;                // packed bytes per weight row and slab
+  constexpr int kRowBytes = kMx ? kSlabK : kSlabK / 2; // weight bytes per row and slab
   constexpr int kRowsPerDma = 1024 / kRowBytes;        // weight rows per 1 KB LDS-DMA
   constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row and slab
   constexpr int kABytes = 2 * kTileRows * kRowBytes;   // weight bytes per slab (128 rows)
   constexpr int kScStride = kTileRows * kMaxGpr * 2;   // bytes per row set (fp16 scales)
   constexpr int kZpStride = kTileRows * kMaxGpr;       // bytes per row set (u8 zeros)
+  constexpr int kADma = kABytes / 1024;                // weight DMAs per slab
+  static_assert(kADma == 4 || kADma == 8 || kADma == 16, "weight DMAs per slab");
   __shared__ __align__(16) unsigned char ring[kRingBytes];
   __shared__ __align__(16) unsigned char ssh[2 * kScStride];
   __shared__ __align__(16) unsigned char szz[2 * kZpStride];
@@ -177,7 +180,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
   const int n = lane & 15, lq = lane >> 4;
   const int ntasks = p.nblk * p.ntile;
   const int npad = p.num_padded[0];
-  const int words = p.K >> 3, gpr = p.K / p.g;
+  const int row_bytes = kMx ? p.K : p.K / 2, gpr = p.K / p.g;
+  constexpr int kScBytes = kMx ? 1 : 2;                 // E8M0 byte or fp16 scale
   const int nslab = p.K / kSlabK;
   const uint32_t nib_mask = in_vgpr(0x000F000Fu);
 
@@ -222,11 +226,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
     const int slot_bytes = kABytes + nbdma * 1024;
     const int depth_fit = kRingBytes / slot_bytes;
     const int depth = depth_fit < kMaxDepth ? depth_fit : kMaxDepth;   // >= 2 by construction
-    constexpr int kADma = kABytes / 1024;                       // weight DMAs per slab
     // This wave's DMAs per slab: weight DMA i goes to wave i, activation DMA
     // i to wave i % 8.
     const int my_b = nbdma > wave ? (nbdma - wave + kGemmWaves - 1) / kGemmWaves : 0;
-    const int per_slab = my_b + (wave < kADma ? 1 : 0);
+    // Weight DMA m goes to wave m % 8 (kADma is 4, 8 or 16).
+    constexpr int kAMax = (kADma + kGemmWaves - 1) / kGemmWaves;   // weight DMAs per wave, at most
+    const int my_a = kADma >= kGemmWaves ? kADma / kGemmWaves : (wave < kADma ? 1 : 0);
+    const int per_slab = my_b + my_a;
 
     // Everything before this point is a plain load the compiler waits for;
     // from here on the only vector-memory operations are the LDS-DMA loads
@@ -240,9 +246,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
 #pragma unroll
     for (int set = 0; set < 2; ++set) {
       const size_t r0 = ebase + static_cast<size_t>(set) * p.set_stride;
-      const int nsc = (kTileRows * gpr * 2) / 16, nzp = (kTileRows * gpr) / 16;
-      const unsigned char* gsc = reinterpret_cast<const unsigned char*>(p.sc + r0 * gpr);
-      const unsigned char* gzp = p.zp + r0 * gpr;
+      const int nsc = (kTileRows * gpr * kScBytes) / 16, nzp = kMx ? 0 : (kTileRows * gpr) / 16;
+      const unsigned char* gsc = p.sc + r0 * gpr * kScBytes;
+      const unsigned char* gzp = kMx ? p.sc : p.zp + r0 * gpr;
       const int w0 = set * 4;
       for (int m = wave - w0; m >= 0 && m < 4 && m * kWave < nsc; m += 4) {
         const int c = m * kWave + lane;
@@ -254,14 +260,16 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
       }
     }
 
-    // Weight DMA of this wave (if any): rows kRowsPerDma * wave + l % kRowsPerDma
-    // of the tile, chunk l / kRowsPerDma of the slab.
-    const uint32_t* qa = nullptr;
-    if (wave < kADma) {
-      const int tr = kRowsPerDma * wave + lane % kRowsPerDma;     // tile-local row
+    // Weight DMAs of this wave: DMA m covers tile rows kRowsPerDma * m ..
+    // +kRowsPerDma-1; lane l takes row l % kRowsPerDma, chunk l / kRowsPerDma.
+    const unsigned char* qa[kAMax];
+#pragma unroll
+    for (int t = 0; t < kAMax; ++t) {
+      const int m = wave + kGemmWaves * t;
+      const int tr = kRowsPerDma * (m < kADma ? m : 0) + lane % kRowsPerDma;     // tile-local row
       const int ch = lane / kRowsPerDma;
       const size_t grow = ebase + static_cast<size_t>(tr / kTileRows) * p.set_stride + tr % kTileRows;
-      qa = p.q + grow * words + 4 * ch;
+      qa[t] = p.q + grow * row_bytes + 16 * ch;
     }
     // This wave's activation DMAs (at most two per slab: nbdma <= 16):
     // DMA i = ((plane * nact + u) * kSteps + j) is issued by wave i % 8 and
@@ -287,15 +295,20 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
     const int ring_used = depth * slot_bytes;
     const uint16_t* bnext0 = bsrc[0];
     const uint16_t* bnext1 = bsrc[1];
-    const uint32_t* anext = qa;
+    const unsigned char* anext[kAMax];
+#pragma unroll
+    for (int t = 0; t < kAMax; ++t) anext[t] = qa[t];
     auto issue_next = [&](int off) {
       unsigned char* slot = ring + off;
       if (my_b > 0) dma16(bnext0, lds_addr(slot + boff[0]));
       if (my_b > 1) dma16(bnext1, lds_addr(slot + boff[1]));
-      if (wave < kADma) dma16(anext, lds_addr(slot + wave * 1024));
+#pragma unroll
+      for (int t = 0; t < kAMax; ++t) {
+        if (t < my_a) dma16(anext[t], lds_addr(slot + (wave + kGemmWaves * t) * 1024));
+        anext[t] += kRowBytes;
+      }
       bnext0 += kSlabK;
       bnext1 += kSlabK;
-      anext += kSlabK / 8;
     };
 
     floatx4 acc[kMaxSub];            // per active index u (sub-tile act[u])
@@ -303,11 +316,16 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
     for (int u = 0; u < kMaxSub; ++u) acc[u] = floatx4{0, 0, 0, 0};
 
     // This lane's weight row within the tile, and where its words sit in a slot.
+    // Step j, lane group q reads elements 32j + 8q .. +7 of the row's slab:
+    // int4 bytes 16j + 4q (word q of chunk j), MXFP8 bytes 32j + 8q (half
+    // q % 2 of chunk 2j + q / 2); chunk c of row r sits at 16 (r + R c).
     const int arow = 64 * rs + rl + n;
-    const int a_off = (arow / kRowsPerDma) * 1024 + 16 * (arow % kRowsPerDma) + 4 * lq;
+    const int a_off = (arow / kRowsPerDma) * 1024 + 16 * (arow % kRowsPerDma) +
+                      (kMx ? 16 * kRowsPerDma * (lq >> 1) + 8 * (lq & 1) : 4 * lq);
+    constexpr int kAStep = kMx ? 32 * kRowsPerDma : 16 * kRowsPerDma;   // LDS bytes per step
     // Scale and zero addresses of this lane (group 0); the group index is
     // added per partial.
-    const uint16_t* sp = reinterpret_cast<const uint16_t*>(ssh + rs * kScStride) + (rl + 4 * lq) * gpr;
+    const unsigned char* sp = ssh + rs * kScStride + (rl + 4 * lq) * gpr * kScBytes;
     const unsigned char* zpl = szz + rs * kZpStride + (rl + n) * gpr;
     // Group of the first partial of a slab: slab s covers groups s * gps ..
     // (g below the slab) or group s / spg (g a multiple of the slab).
@@ -334,20 +352,42 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
       rd += slot_bytes;
       if (rd == ring_used) rd = 0;
       // Step j, lane group q: word 4j + q of the row = word q of chunk j.
-      uint32_t aw[kSteps];
+      uint32_t aw[kSteps][kMx ? 2 : 1];
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j)
-        aw[j] = *reinterpret_cast<const uint32_t*>(slot + a_off + 16 * kRowsPerDma * j);
+      for (int j = 0; j < kSteps; ++j) {
+        if constexpr (kMx) {
+          const uint2 v = *reinterpret_cast<const uint2*>(slot + a_off + kAStep * j);
+          aw[j][0] = v.x;
+          aw[j][1] = v.y;
+        } else {
+          aw[j][0] = *reinterpret_cast<const uint32_t*>(slot + a_off + kAStep * j);
+        }
+      }
 #pragma unroll
       for (int f = 0; f < kSteps / kFlush; ++f) {
         const int grp = grp0 + f;
-        const bf16x8 Z = neg_zero_pairs(zpl[grp]);
+        bf16x8 Z;
         float cs[4];
+        if constexpr (kMx) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(sp[i * gpr + grp]);
+          for (int i = 0; i < 4; ++i) cs[i] = e8m0_to_float(sp[i * gpr + grp]);
+        } else {
+          Z = neg_zero_pairs(zpl[grp]);
+          const uint16_t* sp16 = reinterpret_cast<const uint16_t*>(sp);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(sp16[i * gpr + grp]);
+        }
         bf16x8 A[kFlush];
 #pragma unroll
-        for (int jj = 0; jj < kFlush; ++jj) A[jj] = bias_pairs(aw[kFlush * f + jj], nib_mask);
+        for (int jj = 0; jj < kFlush; ++jj) {
+          if constexpr (kMx) {
+            const uint32_t* w = aw[kFlush * f + jj];
+            A[jj] = __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                                                          fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])));
+          } else {
+            A[jj] = bias_pairs(aw[kFlush * f + jj][0], nib_mask);
+          }
+        }
 #pragma unroll
         for (int u = 0; u < kMaxSub; ++u) {
           if (u >= nact) break;
@@ -362,7 +402,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_int4(const GemmPara
               const bf16x8 B = __builtin_bit_cast(
                   bf16x8, *reinterpret_cast<const uint4*>(slot + kABytes + (((pl * nact + u) * kSteps + j) * 1024) + 16 * lane));
               d = mfma_bf16(A[jj], B, d);
-              d = mfma_bf16(Z, B, d);
+              if constexpr (!kMx) d = mfma_bf16(Z, B, d);
             }
           }
 #pragma unroll
@@ -461,20 +501,31 @@ bool group_ok(int K, int g, int slab) {
   return g < slab ? (slab % g) == 0 : (g % slab) == 0;
 }
 
-template <bool kGateUp, int kPlanes, int kSteps>
-hipError_t launch_gemm(const GemmParams& gp, int wgs, hipStream_t stream) {
+template <int kFmt, bool kGateUp, int kPlanes, int kSteps>
+hipError_t launch_gemm_fmt(const GemmParams& gp, int wgs, hipStream_t stream) {
   switch (flush_steps(gp.g, kSteps)) {
     case 1:
-      hipLaunchKernelGGL((grouped_gemm_int4<kGateUp, kPlanes, kSteps, 1>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 1>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
       break;
     case 2:
-      hipLaunchKernelGGL((grouped_gemm_int4<kGateUp, kPlanes, kSteps, 2>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 2>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm_int4<kGateUp, kPlanes, kSteps, kSteps>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, kSteps>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool kGateUp, int kPlanes, int kSteps>
+hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t stream) {
+  // MXFP8 blocks are 32 elements: one scaled partial per MFMA step.
+  if (fmt == MOE_W_MXFP8) {
+    hipLaunchKernelGGL((grouped_gemm<MOE_W_MXFP8, kGateUp, kPlanes, kSteps, 1>), dim3(wgs), dim3(kGemmThreads), 0,
+                       stream, gp);
+    return hipGetLastError();
+  }
+  return launch_gemm_fmt<MOE_W_INT4_AWQ, kGateUp, kPlanes, kSteps>(gp, wgs, stream);
 }
 
 constexpr int kGateUpSteps = 4;   // 128-element slabs
@@ -482,13 +533,15 @@ constexpr int kDownSteps = 2;     // 64-element slabs (two planes of activations
 
 }  // namespace
 
-bool grouped_shape_ok(int H, int I, int b, int g13, int g2) {
+bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2) {
   // Whole slabs and whole tiles in both GEMMs (gate/up: 64 neurons; down:
-  // 128 rows); the tile's scales and zeros (at most 32 groups per row) are
-  // staged in LDS.
-  return b >= 1 && b <= kMaxTok && (H % 128) == 0 && (I % 64) == 0 && (H % (32 * kGateUpSteps)) == 0 &&
-         (I % (32 * kDownSteps)) == 0 && group_ok(H, g13, 32 * kGateUpSteps) &&
-         group_ok(I, g2, 32 * kDownSteps);
+  // 128 rows); the tile's scales (and int4 zeros) are staged in LDS: int4 at
+  // most 32 groups per row, MXFP8 at most 64 blocks of 32 per row.
+  if (b < 1 || b > kMaxTok || (H % 128) != 0 || (I % 64) != 0 || (H % (32 * kGateUpSteps)) != 0 ||
+      (I % (32 * kDownSteps)) != 0)
+    return false;
+  if (fmt == MOE_W_MXFP8) return g13 == 32 && g2 == 32 && H / 32 <= 2 * kMaxGpr && I / 32 <= 2 * kMaxGpr;
+  return group_ok(H, g13, 32 * kGateUpSteps) && group_ok(I, g2, 32 * kDownSteps);
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
@@ -498,8 +551,8 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.sorted = p.sorted;
   gp.blocks = p.blocks;
   gp.num_padded = p.num_padded;
-  gp.q = static_cast<const uint32_t*>(p.w13.q);
-  gp.sc = static_cast<const uint16_t*>(p.w13.scale);
+  gp.q = static_cast<const unsigned char*>(p.w13.q);
+  gp.sc = static_cast<const unsigned char*>(p.w13.scale);
   gp.zp = p.w13.zero;
   gp.a_hi = p.a_hi;
   gp.a_lo = p.a_lo;
@@ -516,7 +569,7 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.K = p.H;
   gp.g = p.w13.group;
   const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
-  return launch_gemm<true, 1, kGateUpSteps>(gp, wgs, stream);
+  return launch_gemm<true, 1, kGateUpSteps>(p.w13.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
@@ -526,8 +579,8 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.sorted = p.sorted;
   gp.blocks = p.blocks;
   gp.num_padded = p.num_padded;
-  gp.q = static_cast<const uint32_t*>(p.w2.q);
-  gp.sc = static_cast<const uint16_t*>(p.w2.scale);
+  gp.q = static_cast<const unsigned char*>(p.w2.q);
+  gp.sc = static_cast<const unsigned char*>(p.w2.scale);
   gp.zp = p.w2.zero;
   gp.yhat = p.yhat;
   gp.mk = p.M * p.k;
@@ -543,7 +596,7 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.K = p.I;
   gp.g = p.w2.group;
   const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
-  return launch_gemm<false, 2, kDownSteps>(gp, wgs, stream);
+  return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream) {

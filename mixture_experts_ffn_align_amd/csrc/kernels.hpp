@@ -26,7 +26,7 @@ struct DecodeArgs {
   int M, H, I, E, k;
   int max_workgroups;
 };
-bool decode_shape_ok(int H, int I, int k, int g13, int g2);
+bool decode_shape_ok(int fmt, int H, int I, int k, int g13, int g2);
 hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream);
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream);
 
@@ -47,7 +47,7 @@ struct GroupedArgs {
   int nblk;        // blocks in the alignment buffers (capacity / b)
   int max_workgroups;
 };
-bool grouped_shape_ok(int H, int I, int b, int g13, int g2);
+bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2);
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream);

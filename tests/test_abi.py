@@ -144,7 +144,11 @@ def test_forward_validation_enqueues_nothing():
                                       10**9, None, ev, 2) == B.MOE_ERR_INVALID_ARG
 
 
-def test_mxfp8_not_yet_supported():
-    d = B.make_desc(64, 2048, 768, 128, 8, 16, _w(B.MOE_W_MXFP8, 32, z=None),
-                    _w(B.MOE_W_MXFP8, 32, z=None), B.MOE_PATH_AUTO, 0)
-    assert _ws_status(d) == B.MOE_ERR_UNSUPPORTED
+def test_mxfp8_descriptor_rules():
+    # MXFP8 weights: E4M3 codes with an E8M0 exponent per 32 elements, no zeros.
+    mx = lambda g=32: _w(B.MOE_W_MXFP8, g, z=None)
+    for path in (B.MOE_PATH_AUTO, B.MOE_PATH_DECODE, B.MOE_PATH_GROUPED):
+        d = B.make_desc(64, 2048, 768, 128, 8, 16, mx(), mx(), path, 0)
+        assert _ws_status(d) == B.MOE_OK
+    d = B.make_desc(64, 2048, 768, 128, 8, 16, mx(64), mx(64), B.MOE_PATH_AUTO, 0)
+    assert _ws_status(d) == B.MOE_ERR_INVALID_ARG               # blocks are 32 elements

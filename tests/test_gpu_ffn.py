@@ -32,7 +32,7 @@ def _check_intermediate(dw, st, path):
     assert err["rel_l2"] < 1e-4, err
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_m1", "batch_m21", "batch_m256_zipf"])
+@pytest.mark.parametrize("name", ["tiny", "decode_m1", "batch_m21", "batch_m256_zipf", "mxfp8_m64"])
 @pytest.mark.parametrize("path", ["decode", "grouped"])
 def test_ffn_parity_full_size(name, path):
     g = _gpu()
@@ -67,10 +67,15 @@ RAGGED = [
     dict(M=2, H=256, I=1536, E=16, k=12, b=8, g=128),
     # A group spanning two 128-element slabs.
     dict(M=6, H=512, I=256, E=8, k=2, b=16, g=256),
+    # MXFP8 weights (E4M3 + E8M0 per 32): several lane layouts, k > 8, full blocks.
+    dict(M=5, H=256, I=128, E=8, k=2, b=8, g=32, fmt="mxfp8"),
+    dict(M=3, H=512, I=448, E=16, k=5, b=8, g=32, fmt="mxfp8"),
+    dict(M=2, H=384, I=2176, E=16, k=12, b=8, g=32, fmt="mxfp8"),
+    dict(M=70, H=1024, I=256, E=16, k=6, b=64, g=32, fmt="mxfp8"),
 ]
 
 
-@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "M{M}_H{H}_I{I}_E{E}_k{k}_b{b}_g{g}".format(**s))
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "M{M}_H{H}_I{I}_E{E}_k{k}_b{b}_g{g}".format(**s) + ("_mx" if s.get("fmt") == "mxfp8" else ""))
 @pytest.mark.parametrize("path", ["decode", "grouped"])
 def test_ffn_parity_ragged(shape, path):
     g = _gpu()
