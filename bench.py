@@ -33,6 +33,51 @@ N_ROUTINGS = 64
 FLOPS_PER_ROUTE = None  # set from the shapes: 2 * (2I*H + H*I)
 
 
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_counters.json")
+KERNEL_SOURCES = {
+    # kernel family -> sources its code is built from
+    "decode": ["decode.hip", "common.hpp"],
+    "grouped": ["grouped.hip", "common.hpp"],
+}
+
+
+def source_hash(family):
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mixture_experts_ffn_align_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, family):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    FETCH_SIZE / WRITE_SIZE counter passes (calibrated on a plain copy), or
+    None when there is no record or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("kernels", {}).get(f"{workload}:{kernel}")
+    if not entry or entry.get("source_hash") != source_hash(family):
+        return None
+    return int(entry["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+    n = 64 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 20}), flush=True)
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -46,6 +91,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the M=21 / M=256 context numbers")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 64 MiB device copy (the counter calibration kernel) and exit")
     return p.parse_args()
 
 
@@ -238,6 +285,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import mixture_experts_ffn_align_amd as moe
     moe.lib()  # fail loudly if the HIP library is missing
 
@@ -263,8 +313,9 @@ def main():
     names = {"gate_up": moe.moe_ffn_kernel_name(d, 0 if path == "decode" else 1),
              "down_combine": moe.moe_ffn_kernel_name(d, 1 if path == "decode" else 2)}
     achieved = stage_bytes[dom] / (st_us[dom] * 1e-6) / 1e9
+    traffic = measured_traffic(names[dom], cfg.name, path)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": names[dom], "kernel_us": round(st_us[dom], 3),
                 "algorithmic_bytes": int(stage_bytes[dom]),
                 "stage_us": {k: round(v, 3) for k, v in st_us.items()},
@@ -272,7 +323,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name in ("batch_m21", "batch_m256_zipf"):
+        for name in ("batch_m21", "batch_m256_zipf", "mxfp8_m64"):
             log("context workload", name)
             r2 = Rotation(name, 8, 16)
             extra[name] = {k: (round(v, 4) if isinstance(v, float) else v)

@@ -295,8 +295,10 @@ int32_t moe_ffn_kernel_count(const moe_ffn_desc* d) {
 const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i) {
   Layout L;
   if (validate(d, &L, false) != MOE_OK) return nullptr;
-  static const char* const kDecode[] = {"decode_gate_up_int4", "decode_down_int4"};
-  static const char* const kGrouped[] = {"align_kernel", "grouped_gate_up_int4", "grouped_down_int4",
+  // Kernel template names as a kernel trace shows them (before the template
+  // arguments); the grouped GEMM is one template run for both projections.
+  static const char* const kDecode[] = {"decode_gate_up", "decode_down"};
+  static const char* const kGrouped[] = {"align_kernel", "grouped_gemm (gate/up)", "grouped_gemm (down)",
                                          "combine_topk"};
   if (L.path == MOE_PATH_DECODE) return (i >= 0 && i < 2) ? kDecode[i] : nullptr;
   return (i >= 0 && i < 4) ? kGrouped[i] : nullptr;

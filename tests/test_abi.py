@@ -84,8 +84,9 @@ def test_workspace_size_decode_and_grouped():
     off, lo, fmt = moe.moe_ffn_intermediate(d)
     assert fmt == 1 and lo >= off + 8 * 768 * 2
     assert [moe.moe_ffn_kernel_name(dg, i) for i in range(4)] == [
-        "align_kernel", "grouped_gate_up_int4", "grouped_down_int4", "combine_topk"]
+        "align_kernel", "grouped_gemm (gate/up)", "grouped_gemm (down)", "combine_topk"]
     assert moe.moe_ffn_kernel_name(dg, 4) is None
+    assert [moe.moe_ffn_kernel_name(d, i) for i in range(2)] == ["decode_gate_up", "decode_down"]
 
 
 def test_auto_path_threshold():
