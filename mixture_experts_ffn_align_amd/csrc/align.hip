@@ -12,7 +12,10 @@
 //      its equal-expert peers below it. Per-wave counts in LDS give the
 //      offset of earlier waves, and a per-expert running count the offset of
 //      earlier chunks, so each expert's routes land in ascending route ID;
-//   4. padding rows get the sentinel M*k, blocks past num_padded get -1.
+//   4. padding rows keep the sentinel M*k and blocks past num_padded keep -1
+//      from a coalesced prefill at the start (ordered before the placement
+//      by the workgroup barriers in between); each expert writes its own
+//      entries of the block vector.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,16 +27,6 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 
 __device__ __forceinline__ int padded_count(int c, int b) { return (c + b - 1) / b * b; }
-
-// Expert whose aligned rows contain row p (0 <= p < off[E]): off[lo] <= p < off[lo+1].
-__device__ __forceinline__ int expert_of_row(const int* off, int E, int p) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (off[mid] <= p) lo = mid; else hi = mid;
-  }
-  return lo;
-}
 
 __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int mk, int E, int b, int nbits,
@@ -47,7 +40,12 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   uint8_t* wcnt = reinterpret_cast<uint8_t*>(wtot + 32);  // [16][E] per-wave counts in a chunk
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nblk = cap / b;
 
+  // Prefill: every row is padding and every block is past the end until the
+  // steps below overwrite them (the ids loads are in flight meanwhile).
+  for (int p = tid; p < cap; p += kThreads) sorted[p] = mk;
+  for (int i = tid; i < nblk; i += kThreads) blocks[i] = -1;
   for (int e = tid; e < E; e += kThreads) { cnt[e] = 0; run[e] = 0; }
   for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
   __syncthreads();
@@ -96,6 +94,10 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     num_padded[0] = total;
   }
   __syncthreads();
+  // Block vector: expert e owns blocks off[e]/b .. off[e+1]/b - 1.
+  for (int e = tid; e < E; e += kThreads) {
+    for (int p = off[e]; p < off[e + 1]; p += b) blocks[p / b] = e;
+  }
 
   // Stable placement, one chunk of 1024 routes at a time.
   const unsigned long long below = (1ull << lane) - 1ull;
@@ -125,21 +127,6 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
       wcnt[wave * E + e] = 0;
     }
     __syncthreads();
-  }
-
-  // Padding and tails. These rows are disjoint from the rows written above.
-  for (int p = tid; p < cap; p += kThreads) {
-    if (p >= total) {
-      sorted[p] = mk;
-    } else {
-      const int e = expert_of_row(off, E, p);
-      if (p - off[e] >= cnt[e]) sorted[p] = mk;
-    }
-  }
-  const int nblk = cap / b;
-  for (int i = tid; i < nblk; i += kThreads) {
-    const int p = i * b;
-    blocks[i] = p < total ? expert_of_row(off, E, p) : -1;
   }
 }
 
