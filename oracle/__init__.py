@@ -23,7 +23,10 @@ alignment invariants, dequantisation on hand-built words and on all 16 x 16
 case against a dense SwiGLU built from torch's float64 ``matmul`` and
 ``silu``, zero input giving exact zeros, linearity in the combine weights,
 W2 scale doubling, invalid-ID skipping, and all 256 E4M3 codes against
-``torch.float8_e4m3fn``. Every function below is pinned by at least one of
+``torch.float8_e4m3fn``. The expert-range form (only experts [expert_base,
+expert_base + E) held here) is pinned by hand-worked range fixtures, the
+sort-based brute force with a range, disjoint shards partitioning the routes,
+the loop FFN with a range, and shard outputs summing to the full layer. Every function below is pinned by at least one of
 these; none is "parity unpinned".
 """
 from .moe_oracle import (  # noqa: F401

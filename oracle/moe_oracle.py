@@ -38,18 +38,20 @@ def align_capacity(M: int, k: int, E: int, b: int) -> int:
     return ((raw + b - 1) // b) * b
 
 
-def align(topk_ids: np.ndarray, E: int, b: int, capacity: int | None = None):
+def align(topk_ids: np.ndarray, E: int, b: int, capacity: int | None = None,
+          expert_base: int = 0):
     """Stable route alignment.
 
     Route IDs r are the row-major flattening of the M x k expert-ID array
     (r = t*k + j) [P1, first paragraph]. A route is valid when its expert ID
-    lies in [0, E); invalid routes are skipped. For each expert e in
-    ascending order, its valid routes are listed in ascending route ID
+    lies in [expert_base, expert_base + E) — the E experts held here, all of
+    them when expert_base is 0; invalid routes are skipped. For each expert e
+    in ascending order, its valid routes are listed in ascending route ID
     (ordering by (expert ID, flattened route ID) [P1, stable construction]),
     then padded with the sentinel M*k up to ceil(c_e / b) * b rows; each
-    group of b rows is one block whose entry in the expert-block vector is e
-    [P1, first paragraph; A_e / B(e, j) paragraph]. Experts with no routes
-    get no rows.
+    group of b rows is one block whose entry in the expert-block vector is
+    the expert's local index e - expert_base [P1, first paragraph; A_e /
+    B(e, j) paragraph]. Experts with no routes get no rows.
 
     Returns (sorted_route_ids int32 [C], expert_block_ids int32 [C / b],
     num_padded int) with C = ``capacity`` (default ``align_capacity``).
@@ -68,7 +70,7 @@ def align(topk_ids: np.ndarray, E: int, b: int, capacity: int | None = None):
     blocks = np.full(C // b, -1, dtype=np.int32)
     off = 0
     for e in range(E):
-        routes = np.nonzero(ids == e)[0]          # ascending route IDs
+        routes = np.nonzero(ids == expert_base + e)[0]    # ascending route IDs
         c = routes.size
         if c == 0:
             continue
@@ -175,9 +177,12 @@ def _silu(v: np.ndarray) -> np.ndarray:
 
 
 def ffn_stages(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
-               w13, w2, E: int) -> dict:
+               w13, w2, E: int, expert_base: int = 0) -> dict:
     """All intermediate surfaces of the layer in float64.
 
+    A route is valid when its expert ID lies in [expert_base, expert_base +
+    E); the weights hold those E experts, expert ID e at index e -
+    expert_base (expert_base = 0: all experts).
     For each valid route r (token t = r // k, expert e = ids[r]):
       gate = W13[e, 0:I, :] x_t,  up = W13[e, I:2I, :] x_t   (W13 rows 0..I-1
       are the gate projection, I..2I-1 the up projection),
@@ -205,11 +210,11 @@ def ffn_stages(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
     a = np.zeros((M * k, I))
     yhat = np.zeros((M * k, H))
     for e in np.unique(flat):
-        if e < 0 or e >= E:
+        if e < expert_base or e >= expert_base + E:
             continue
         routes = np.nonzero(flat == e)[0]
-        W13 = _dequant(w13, int(e))          # [2I, H]
-        W2 = _dequant(w2, int(e))            # [H, I]
+        W13 = _dequant(w13, int(e - expert_base))          # [2I, H]
+        W2 = _dequant(w2, int(e - expert_base))            # [H, I]
         X = x[routes // k]                   # [n, H]
         G = X @ W13[:I].T
         U = X @ W13[I:].T
@@ -222,11 +227,11 @@ def ffn_stages(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
     for t in range(M):
         for j in range(k):
             e = ids[t, j]
-            if 0 <= e < E:
+            if expert_base <= e < expert_base + E:
                 y[t] += wts[t, j] * yhat[t * k + j]
     return {"gate": gate, "up": up, "a": a, "yhat": yhat, "y": y}
 
 
-def ffn(x_bits, topk_ids, topk_w, w13, w2, E: int) -> np.ndarray:
+def ffn(x_bits, topk_ids, topk_w, w13, w2, E: int, expert_base: int = 0) -> np.ndarray:
     """Layer output y [M, H] in float64 (see ``ffn_stages``)."""
-    return ffn_stages(x_bits, topk_ids, topk_w, w13, w2, E)["y"]
+    return ffn_stages(x_bits, topk_ids, topk_w, w13, w2, E, expert_base)["y"]

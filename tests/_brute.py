@@ -8,11 +8,12 @@ import math
 import struct
 
 
-def brute_align(topk_ids, E, b, capacity):
-    """Sort-based alignment: valid routes sorted by (expert ID, route ID)."""
+def brute_align(topk_ids, E, b, capacity, base=0):
+    """Sort-based alignment: valid routes (expert ID in [base, base + E))
+    sorted by (expert ID, route ID); block entries are local indices."""
     flat = [int(e) for row in topk_ids for e in row]
     mk = len(flat)
-    valid = [r for r in range(mk) if 0 <= flat[r] < E]
+    valid = [r for r in range(mk) if base <= flat[r] < base + E]
     order = sorted(valid, key=lambda r: (flat[r], r))
     rows, blocks = [], []
     i = 0
@@ -25,7 +26,7 @@ def brute_align(topk_ids, E, b, capacity):
         while len(seg) % b:
             seg = seg + [mk]
         rows.extend(seg)
-        blocks.extend([e] * (len(seg) // b))
+        blocks.extend([e - base] * (len(seg) // b))
         i = j
     n = len(rows)
     rows += [mk] * (capacity - n)
@@ -45,8 +46,9 @@ def deq_elem(q, s, z, g, e, n, kk):
     return (nib - int(z[e][n][kk // g])) * float(s[e][n][kk // g])
 
 
-def brute_ffn(x_bits, topk_ids, topk_w, w13, w2, E):
-    """y[t][h] by explicit loops over tokens, routes, neurons and elements."""
+def brute_ffn(x_bits, topk_ids, topk_w, w13, w2, E, base=0):
+    """y[t][h] by explicit loops over tokens, routes, neurons and elements;
+    expert ID e is valid in [base, base + E) and uses weight index e - base."""
     M = len(topk_ids)
     k = len(topk_ids[0])
     H = len(x_bits[0])
@@ -57,7 +59,7 @@ def brute_ffn(x_bits, topk_ids, topk_w, w13, w2, E):
     for t in range(M):
         x = [bf16_bits_to_float(v) for v in x_bits[t]]
         for j in range(k):
-            e = int(topk_ids[t][j])
+            e = int(topk_ids[t][j]) - base
             if not (0 <= e < E):
                 continue
             wt = float(topk_w[t][j])

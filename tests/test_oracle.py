@@ -30,12 +30,13 @@ def _load(name):
 # Alignment
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", _load("align_hand_worked.json")["cases"], ids=lambda c: c["name"])
+@pytest.mark.parametrize("case", _load("align_hand_worked.json")["cases"] +
+                         _load("align_expert_range_hand_worked.json")["cases"], ids=lambda c: c["name"])
 def test_align_hand_worked(case):
     ids = np.array(case["topk_ids"], dtype=np.int32)
     cap = oracle.align_capacity(case["M"], case["k"], case["E"], case["b"])
     assert cap == case["capacity"]
-    got = oracle.align(ids, case["E"], case["b"])
+    got = oracle.align(ids, case["E"], case["b"], expert_base=case.get("expert_base", 0))
     ref = (case["sorted_route_ids"], case["expert_block_ids"], case["num_padded"])
     assert alignment_mismatch(got, ref) is None
 
@@ -64,6 +65,41 @@ def test_align_vs_sort_brute_force(E, b):
         got = oracle.align(ids, E, b)
         ref = _brute.brute_align(ids.tolist(), E, b, cap)
         assert alignment_mismatch(got, ref) is None
+
+
+@pytest.mark.parametrize("E_total,E,base", [(8, 8, 0), (8, 3, 2), (128, 16, 64), (257, 1, 256),
+                                            (16, 4, 20)])
+@pytest.mark.parametrize("b", [1, 8, 64])
+def test_align_expert_range_vs_sort_brute_force(E_total, E, base, b):
+    # Only experts in [base, base + E) are held here; the rest are invalid.
+    rng = np.random.default_rng(E_total * 7 + base * 3 + b)
+    for trial in range(3):
+        M = int(rng.integers(1, 40))
+        k = int(min(E_total, rng.integers(1, 9)))
+        ids = _random_ids(rng, M, k, E_total, invalid_frac=0.1 * trial, distinct=trial != 2)
+        cap = oracle.align_capacity(M, k, E, b)
+        got = oracle.align(ids, E, b, expert_base=base)
+        ref = _brute.brute_align(ids.tolist(), E, b, cap, base=base)
+        assert alignment_mismatch(got, ref) is None
+
+
+def test_align_expert_range_shards_partition_the_routes():
+    # Aligning each of four 32-expert shards separately places every valid
+    # route exactly once, in the same per-expert order as the full alignment.
+    rng = np.random.default_rng(11)
+    ids = rng.integers(0, 128, size=(300, 8)).astype(np.int32)
+    full_s, full_b, full_n = oracle.align(ids, 128, 16)
+    seen = []
+    for shard in range(4):
+        s, blocks, n = oracle.align(ids, 32, 16, expert_base=32 * shard)
+        rows = s[:n]
+        seen.extend(int(r) for r in rows if r != ids.size)
+        for blk in range(n // 16):
+            e = 32 * shard + int(blocks[blk])
+            got = [int(r) for r in rows[blk * 16:(blk + 1) * 16] if r != ids.size]
+            assert all(ids.reshape(-1)[r] == e for r in got)
+    assert sorted(seen) == list(range(ids.size))
+    assert sum(oracle.align(ids, 32, 16, expert_base=32 * s)[2] for s in range(4)) == full_n
 
 
 def test_align_b1_is_stable_argsort():
@@ -227,6 +263,36 @@ def test_ffn_matches_loop_brute_force_invalid_ids_and_small_groups():
     yb = np.array(_brute.brute_ffn(wl.x.tolist(), wl.topk_ids.tolist(), wl.topk_w.tolist(),
                                    wl.w13, wl.w2, cfg.E))
     np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12 * np.abs(yb).max())
+
+
+def test_ffn_expert_range_matches_loop_brute_force():
+    # Experts [2, 5) of a 7-expert model held here: the local weights are
+    # experts 2..4, IDs outside the range are skipped.
+    cfg = _tiny_cfg(M=4, H=64, I=32, E=3, k=3, g=32)
+    wl = make_workload(cfg, seed=4)
+    rng = np.random.default_rng(4)
+    ids = np.stack([rng.permutation(7)[:3] for _ in range(4)]).astype(np.int32)
+    y = oracle.ffn(wl.x, ids, wl.topk_w, wl.w13, wl.w2, 3, expert_base=2)
+    yb = np.array(_brute.brute_ffn(wl.x.tolist(), ids.tolist(), wl.topk_w.tolist(),
+                                   wl.w13, wl.w2, 3, base=2))
+    assert np.abs(yb).max() > 0
+    np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12 * np.abs(yb).max())
+
+
+def test_ffn_expert_shards_sum_to_the_full_layer():
+    # The layer is linear in the per-expert outputs: the outputs of disjoint
+    # expert shards (each with its slice of the weights) add up to the
+    # output of the full layer.
+    wl = make_workload("tiny", seed=5)
+    E = wl.cfg.E
+
+    def shard(pw, lo, hi):
+        return PackedWeights(pw.fmt, pw.N, pw.K, pw.g, pw.q[lo:hi], pw.s[lo:hi],
+                             None if pw.z is None else pw.z[lo:hi])
+    full = oracle.ffn(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, E)
+    parts = sum(oracle.ffn(wl.x, wl.topk_ids, wl.topk_w, shard(wl.w13, lo, lo + 2),
+                           shard(wl.w2, lo, lo + 2), 2, expert_base=lo) for lo in range(0, E, 2))
+    np.testing.assert_allclose(parts, full, rtol=1e-12, atol=1e-12 * np.abs(full).max())
 
 
 def _identical_experts(wl):
