@@ -88,14 +88,19 @@ typedef struct {
   int32_t M;               /* tokens (>= 0) */
   int32_t H;               /* hidden size, multiple of 32 and of w13.group */
   int32_t I;               /* per-expert intermediate size, multiple of 32 and of w2.group */
-  int32_t E;               /* experts (1..2048) */
-  int32_t k;               /* experts per token (1..E) */
+  int32_t E;               /* experts held here (1..2048): IDs expert_base .. expert_base + E - 1 */
+  int32_t k;               /* routes per token (>= 1) */
   int32_t b;               /* alignment block size used by the grouped path (>= 1) */
   moe_weights w13;
   moe_weights w2;
   int32_t path;            /* moe_path */
   int32_t max_workgroups;  /* 0: library default grid. > 0: cap on workgroups per launch.
                               Output bytes do not depend on it. */
+  int32_t expert_base;     /* first expert ID held here (>= 0; 0 for a whole layer). A route
+                              whose ID lies outside [expert_base, expert_base + E) is skipped,
+                              so the E experts of one expert-parallel shard compute that
+                              shard's share of y; w13 / w2 hold those E experts, ID e at
+                              index e - expert_base. */
 } moe_ffn_desc;
 
 /* Number of int32 entries sorted_route_ids needs: roundup(M*k + min(E, M*k)*(b-1), b).
@@ -105,7 +110,7 @@ MOE_API size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
 
 /* Step (1), route alignment ("Route-Block Membership Selects Packed-AWQ
  * Arithmetic": first paragraph; A_e / B(e,j) paragraph; stable-construction
- * paragraph).
+ * paragraph). Same as moe_align_ex with expert_base 0 and no workspace.
  *   topk_ids          [M*k] int32, row-major [M][k]
  *   sorted_route_ids  [capacity] out: for each expert e ascending, its valid route
  *                     IDs in ascending order, then the sentinel M*k up to a multiple
@@ -118,6 +123,29 @@ MOE_API size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
 MOE_API moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
                      int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
                      size_t capacity, hipStream_t stream);
+
+/* Step (1) for the experts held here and at any size: only routes whose ID
+ * lies in [expert_base, expert_base + E) are valid, and expert_block_ids holds
+ * local indices e - expert_base (an expert-parallel shard aligns its own
+ * routes; the pages' stable order and padding apply unchanged to the valid
+ * routes). Outputs, capacity (with E the number of experts held here) and
+ * errors as moe_align, plus MOE_ERR_INVALID_ARG for expert_base < 0 or
+ * expert_base + E > INT32_MAX, and MOE_ERR_WORKSPACE for a workspace smaller
+ * than moe_align_ex_workspace_size.
+ *   ws, ws_bytes  device scratch (256-byte aligned) of moe_align_ex_workspace_size
+ *                 bytes, or NULL. With it, more than 8192 routes run as three
+ *                 launches over workgroups of 4096 routes (per-workgroup histogram,
+ *                 per-expert prefix over workgroups, stable scatter); without it,
+ *                 or for fewer routes, as one workgroup. The output is the same. */
+MOE_API moe_status moe_align_ex(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E,
+                                int32_t expert_base, int32_t b, int32_t* sorted_route_ids,
+                                int32_t* expert_block_ids, int32_t* num_padded, size_t capacity,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of moe_align_ex for M*k routes over E experts (0 when one
+ * workgroup runs it). Errors: MOE_ERR_INVALID_ARG (null bytes, M < 0, k < 1,
+ * E < 1), MOE_ERR_UNSUPPORTED (E > 2048 or M*k > 2^24). */
+MOE_API moe_status moe_align_ex_workspace_size(int32_t M, int32_t k, int32_t E, size_t* bytes);
 
 /* Bytes of device workspace moe_ffn_forward needs for this description (path
  * resolved as moe_ffn_forward resolves it). Errors as moe_ffn_forward's

@@ -41,7 +41,7 @@ class moe_weights(ctypes.Structure):
 class moe_ffn_desc(ctypes.Structure):
     _fields_ = [("M", _c_i32), ("H", _c_i32), ("I", _c_i32), ("E", _c_i32), ("k", _c_i32),
                 ("b", _c_i32), ("w13", moe_weights), ("w2", moe_weights), ("path", _c_i32),
-                ("max_workgroups", _c_i32)]
+                ("max_workgroups", _c_i32), ("expert_base", _c_i32)]
 
 
 class MoeError(RuntimeError):
@@ -54,6 +54,9 @@ _SIGNATURES = {
     "moe_align_capacity": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "moe_align": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr,
                            _c_size, _c_ptr]),
+    "moe_align_ex": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr,
+                              _c_size, _c_ptr, _c_size, _c_ptr]),
+    "moe_align_ex_workspace_size": (_c_i32, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "moe_ffn_workspace_size": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size)]),
     "moe_ffn_forward": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                  _c_ptr, _c_size, _c_ptr]),
@@ -141,13 +144,32 @@ def moe_align(topk_ids, E: int, b: int, sorted_route_ids, expert_block_ids, num_
     return st
 
 
+def moe_align_ex_workspace_size(M: int, k: int, E: int) -> int:
+    n = _c_size(0)
+    _check(lib().moe_align_ex_workspace_size(M, k, E, ctypes.byref(n)), "moe_align_ex_workspace_size")
+    return int(n.value)
+
+
+def moe_align_ex(topk_ids, E: int, expert_base: int, b: int, sorted_route_ids, expert_block_ids,
+                 num_padded, ws=None, stream=None, check: bool = True) -> int:
+    M, k = topk_ids.shape
+    st = lib().moe_align_ex(_ptr(topk_ids), M, k, E, expert_base, b, _ptr(sorted_route_ids),
+                            _ptr(expert_block_ids), _ptr(num_padded), sorted_route_ids.numel(),
+                            _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                            _stream(stream))
+    if check:
+        _check(st, "moe_align_ex")
+    return st
+
+
 def weights_struct(fmt: int, group: int, q, scale, zero) -> moe_weights:
     return moe_weights(fmt, group, _ptr(q), _ptr(scale), _ptr(zero))
 
 
 def make_desc(M: int, H: int, I: int, E: int, k: int, b: int, w13: moe_weights,
-              w2: moe_weights, path: int = MOE_PATH_AUTO, max_workgroups: int = 0) -> moe_ffn_desc:
-    return moe_ffn_desc(M, H, I, E, k, b, w13, w2, path, max_workgroups)
+              w2: moe_weights, path: int = MOE_PATH_AUTO, max_workgroups: int = 0,
+              expert_base: int = 0) -> moe_ffn_desc:
+    return moe_ffn_desc(M, H, I, E, k, b, w13, w2, path, max_workgroups, expert_base)
 
 
 def moe_ffn_workspace_size(desc: moe_ffn_desc, check: bool = True):

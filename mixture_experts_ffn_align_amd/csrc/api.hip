@@ -28,7 +28,7 @@ size_t capacity_of(int64_t M, int64_t k, int64_t E, int64_t b) {
 struct Layout {
   int path = MOE_PATH_DECODE;
   size_t cap = 0;        // alignment capacity (grouped)
-  size_t off_sorted = 0, off_blocks = 0, off_npad = 0;
+  size_t off_sorted = 0, off_blocks = 0, off_npad = 0, off_align_ws = 0, align_ws = 0;
   size_t off_a = 0, off_a_lo = 0, off_yhat = 0;
   size_t total = 0;
 };
@@ -42,8 +42,8 @@ bool weights_ok(const moe_weights& w) {
 
 moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
-  if (d->M < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->b < 1)
-    return MOE_ERR_INVALID_ARG;
+  if (d->M < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->k < 1 || d->b < 1) return MOE_ERR_INVALID_ARG;
+  if (d->expert_base < 0 || d->expert_base > INT32_MAX - d->E) return MOE_ERR_INVALID_ARG;
   if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_GROUPED) return MOE_ERR_INVALID_ARG;
   if (d->max_workgroups < 0) return MOE_ERR_INVALID_ARG;
   if (d->w13.fmt != d->w2.fmt) return MOE_ERR_INVALID_ARG;
@@ -75,6 +75,8 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   L->off_sorted = o; o += round256(L->cap * sizeof(int32_t));
   L->off_blocks = o; o += round256((L->cap / d->b) * sizeof(int32_t));
   L->off_npad = o;   o += 256;
+  L->align_ws = moe::align_ws_bytes(static_cast<int>(mk), d->E);
+  L->off_align_ws = o; o += L->align_ws;
   L->off_a = o;      o += round256(size_t(mk) * d->I * sizeof(uint16_t));
   L->off_a_lo = o;   o += round256(size_t(mk) * d->I * sizeof(uint16_t));
   L->off_yhat = o;   o += round256(size_t(mk) * d->H * sizeof(float));
@@ -115,6 +117,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
     p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
     p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_a_lo); p.y = y;
     p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k;
+    p.ebase = d->expert_base;
     p.max_workgroups = d->max_workgroups;
     if (stages & kStageGateUp) {
       if ((st = hip_status(moe::launch_decode_gate_up(p, s))) != MOE_OK) return st;
@@ -132,6 +135,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
   p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_a_lo);
   p.yhat = at<float>(ws, L.off_yhat); p.y = y;
   p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k; p.b = d->b;
+  p.ebase = d->expert_base;
   p.max_workgroups = d->max_workgroups;
   if (a_sorted == nullptr) {
     p.sorted = at<int32_t>(ws, L.off_sorted);
@@ -139,9 +143,11 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
     p.num_padded = at<int32_t>(ws, L.off_npad);
     p.nblk = static_cast<int>(L.cap / d->b);
     if (stages & kStageGateUp) {
-      if ((st = hip_status(moe::launch_align(ids, static_cast<int>(mk), d->E, d->b,
+      if ((st = hip_status(moe::launch_align(ids, static_cast<int>(mk), d->E, d->expert_base, d->b,
                                              at<int32_t>(ws, L.off_sorted), at<int32_t>(ws, L.off_blocks),
-                                             at<int32_t>(ws, L.off_npad), static_cast<int>(L.cap), s))) != MOE_OK)
+                                             at<int32_t>(ws, L.off_npad), static_cast<int>(L.cap),
+                                             L.align_ws ? at<void>(ws, L.off_align_ws) : nullptr, L.align_ws,
+                                             s))) != MOE_OK)
         return st;
       if ((st = mark()) != MOE_OK) return st;
     }
@@ -187,10 +193,11 @@ size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b) {
   return capacity_of(M, k, E, b);
 }
 
-moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
-                     int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
-                     size_t capacity, hipStream_t stream) {
+moe_status moe_align_ex(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t expert_base,
+                        int32_t b, int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
+                        size_t capacity, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M < 0 || k < 1 || E < 1 || b < 1) return MOE_ERR_INVALID_ARG;
+  if (expert_base < 0 || expert_base > INT32_MAX - E) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
   if (topk_ids == nullptr || sorted_route_ids == nullptr || expert_block_ids == nullptr ||
       num_padded == nullptr)
@@ -199,8 +206,27 @@ moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, i
   const size_t need = capacity_of(M, k, E, b);
   if (capacity < need) return MOE_ERR_CAPACITY;
   if (capacity > size_t(INT32_MAX)) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_align(topk_ids, M * k, E, b, sorted_route_ids, expert_block_ids,
-                                      num_padded, static_cast<int>(capacity), stream));
+  const size_t ws_need = moe::align_ws_bytes(M * k, E);
+  if (ws_need > 0 && ws != nullptr) {
+    if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < ws_need) return MOE_ERR_WORKSPACE;
+  }
+  return hip_status(moe::launch_align(topk_ids, M * k, E, expert_base, b, sorted_route_ids, expert_block_ids,
+                                      num_padded, static_cast<int>(capacity), ws, ws_bytes, stream));
+}
+
+moe_status moe_align(const int32_t* topk_ids, int32_t M, int32_t k, int32_t E, int32_t b,
+                     int32_t* sorted_route_ids, int32_t* expert_block_ids, int32_t* num_padded,
+                     size_t capacity, hipStream_t stream) {
+  return moe_align_ex(topk_ids, M, k, E, 0, b, sorted_route_ids, expert_block_ids, num_padded, capacity,
+                      nullptr, 0, stream);
+}
+
+moe_status moe_align_ex_workspace_size(int32_t M, int32_t k, int32_t E, size_t* bytes) {
+  if (bytes == nullptr || M < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || int64_t(M) * k > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+  *bytes = moe::align_ws_bytes(M * k, E);
+  return MOE_OK;
 }
 
 moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes) {

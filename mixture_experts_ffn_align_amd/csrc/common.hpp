@@ -79,6 +79,13 @@ __device__ __forceinline__ void unpack8_bias128_m(uint32_t w, uint32_t m, uint32
   p[3] = ((w >> 12) & m) | c;
 }
 
+// Workgroup barrier for LDS data (and control) only. __syncthreads() also
+// fences global memory: it waits for every load and store of the wave in
+// flight (draining a load pipeline, or a store round trip per barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
 // Wave-uniform integer made explicitly scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -113,9 +120,10 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
-// Route-ID gathers that tolerate any value: invalid entries map to -1.
-__device__ __forceinline__ int load_expert(const int32_t* ids, int r, int E) {
-  int e = ids[r];
+// Local expert index of route r: experts [ebase, ebase + E) are held here;
+// any other value (an invalid route) maps to -1.
+__device__ __forceinline__ int load_expert(const int32_t* ids, int r, int E, int ebase) {
+  const int e = ids[r] - ebase;
   return (e >= 0 && e < E) ? e : -1;
 }
 

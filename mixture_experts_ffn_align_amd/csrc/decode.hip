@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ sc,
     const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
-    int mk, int k, int E, int H, int I, int g_shift) {
+    int mk, int k, int E, int ebase, int H, int I, int g_shift) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
   const int lane = threadIdx.x & (kWave - 1);
   // Task indices are wave-uniform: keep them (and the row addresses) scalar.
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
   for (int task = wave_id; task < ntasks; task += nwaves) {
     const int r = task / tasks_per_route;
     const int i0 = (task - r * tasks_per_route) * kNpw;
-    const int e = uniform(load_expert(ids, r, E));
+    const int e = uniform(load_expert(ids, r, E, ebase));
     if (e < 0) {
       if (lane < kNpw) {
         a_hi[static_cast<size_t>(r) * I + i0 + lane] = 0;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ sc,
-    const uint8_t* __restrict__ zp, float* __restrict__ y, int M, int k, int E, int H, int I,
+    const uint8_t* __restrict__ zp, float* __restrict__ y, int M, int k, int E, int ebase, int H, int I,
     int g_shift) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
   constexpr int kSlots = kWave / kSpan;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
       // An invalid route has a zero intermediate (the gate/up kernel writes
       // zeros for it); it reads expert 0's rows and adds exactly zero. No
       // branch here: the compiler would sink the loads above into it.
-      const int e_raw = uniform(load_expert(ids, static_cast<int>(r), E));
+      const int e_raw = uniform(load_expert(ids, static_cast<int>(r), E, ebase));
       const int e = e_raw < 0 ? 0 : e_raw;
       const float wr = e_raw < 0 ? 0.0f : topk_w[r];
       const unsigned char* qt = q + (static_cast<size_t>(e) * H + h0) * row_bytes;
@@ -397,7 +397,7 @@ void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
   hipLaunchKernelGGL((decode_down<kFmt, kCh, kSpan>), dim3(wgs), dim3(kDownThreads), 0, stream,
                      p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const unsigned char*>(p.w2.q),
                      static_cast<const unsigned char*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E,
-                     p.H, p.I, log2_of(p.w2.group));
+                     p.ebase, p.H, p.I, log2_of(p.w2.group));
 }
 
 template <int kFmt>
@@ -434,10 +434,10 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const auto* s = static_cast<const unsigned char*>(p.w13.scale);
   if (p.w13.fmt == MOE_W_MXFP8)
     hipLaunchKernelGGL(decode_gate_up<MOE_W_MXFP8>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q, s,
-                       p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H, p.I, log2_of(p.w13.group));
+                       p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
   else
     hipLaunchKernelGGL(decode_gate_up<MOE_W_INT4_AWQ>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q,
-                       s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.H, p.I, log2_of(p.w13.group));
+                       s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
   return hipGetLastError();
 }
 

@@ -90,12 +90,6 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
-// Workgroup barrier for LDS data only. __syncthreads() also fences global
-// memory, which waits for every load in flight and would drain the rings.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -465,7 +459,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
 
 __global__ __launch_bounds__(kThreads) void combine_topk(
     const float* __restrict__ yhat, const int32_t* __restrict__ ids,
-    const float* __restrict__ topk_w, float* __restrict__ y, int M, int k, int E, int H) {
+    const float* __restrict__ topk_w, float* __restrict__ y, int M, int k, int E, int ebase, int H) {
   const int quads = H >> 2;
   const int total = M * quads;
   for (int i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
@@ -474,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void combine_topk(
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const int r = t * k + j;
-      const int e = ids[r];
+      const int e = ids[r] - ebase;
       if (e < 0 || e >= E) continue;
       const float w = topk_w[r];
       const float4 v = *reinterpret_cast<const float4*>(yhat + static_cast<size_t>(r) * H + h);
@@ -603,7 +597,7 @@ hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream) {
   const int total = p.M * (p.H / 4);
   const int wgs = grid_for((total + kThreads - 1) / kThreads, p.max_workgroups);
   hipLaunchKernelGGL(combine_topk, dim3(wgs), dim3(kThreads), 0, stream, p.yhat, p.ids, p.topk_w,
-                     p.y, p.M, p.k, p.E, p.H);
+                     p.y, p.M, p.k, p.E, p.ebase, p.H);
   return hipGetLastError();
 }
 

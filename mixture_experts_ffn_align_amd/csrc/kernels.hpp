@@ -9,10 +9,16 @@
 
 namespace moe {
 
-// Route alignment (align.hip).
+// Route alignment (align.hip). Up to kAlignSingleMaxRoutes routes run as one
+// workgroup; more (with a workspace of align_ws_bytes) as three launches over
+// workgroups of kAlignRoutesPerGroup routes. Experts [ebase, ebase + E) are
+// held here.
+constexpr int kAlignSingleMaxRoutes = 8192;
+constexpr int kAlignRoutesPerGroup = 4096;
 size_t align_lds_bytes(int E);
-hipError_t launch_align(const int32_t* ids, int mk, int E, int b, int32_t* sorted, int32_t* blocks,
-                        int32_t* num_padded, int cap, hipStream_t stream);
+size_t align_ws_bytes(int mk, int E);
+hipError_t launch_align(const int32_t* ids, int mk, int E, int ebase, int b, int32_t* sorted, int32_t* blocks,
+                        int32_t* num_padded, int cap, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Decode path (decode.hip).
 struct DecodeArgs {
@@ -24,6 +30,7 @@ struct DecodeArgs {
   uint16_t* a_lo;  // bf16 [M*k][I] intermediate, low part
   float* y;        // fp32 [M][H]
   int M, H, I, E, k;
+  int ebase;       // experts [ebase, ebase + E) are held here
   int max_workgroups;
 };
 bool decode_shape_ok(int fmt, int H, int I, int k, int g13, int g2);
@@ -44,6 +51,7 @@ struct GroupedArgs {
   float* yhat;     // fp32 [M*k][H]
   float* y;        // fp32 [M][H]
   int M, H, I, E, k, b;
+  int ebase;       // experts [ebase, ebase + E) are held here
   int nblk;        // blocks in the alignment buffers (capacity / b)
   int max_workgroups;
 };

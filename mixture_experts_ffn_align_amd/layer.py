@@ -52,16 +52,21 @@ class MoeLayer:
     """Routed expert-FFN layer: y = sum_j w[t,j] * FFN_{ids[t,j]}(x_t)."""
 
     def __init__(self, w13: DeviceProjection, w2: DeviceProjection, E: int, H: int, I: int,
-                 k: int, b: int, path: int = B.MOE_PATH_AUTO, max_workgroups: int = 0):
+                 k: int, b: int, path: int = B.MOE_PATH_AUTO, max_workgroups: int = 0,
+                 expert_base: int = 0):
+        """E experts with IDs expert_base .. expert_base + E - 1 (the whole layer
+        when expert_base is 0 and E is the expert count; otherwise one expert-
+        parallel shard, whose output is that shard's share of y)."""
         self.w13, self.w2 = w13, w2
         self.E, self.H, self.I, self.k, self.b = E, H, I, k, b
-        self.path, self.max_workgroups = path, max_workgroups
+        self.path, self.max_workgroups, self.expert_base = path, max_workgroups, expert_base
         self._ws = {}
 
     def desc(self, M: int, path: int | None = None, max_workgroups: int | None = None):
         return B.make_desc(M, self.H, self.I, self.E, self.k, self.b, self.w13.struct(),
                            self.w2.struct(), self.path if path is None else path,
-                           self.max_workgroups if max_workgroups is None else max_workgroups)
+                           self.max_workgroups if max_workgroups is None else max_workgroups,
+                           self.expert_base)
 
     def workspace(self, desc) -> torch.Tensor:
         n = B.moe_ffn_workspace_size(desc)

@@ -26,8 +26,9 @@ W2 scale doubling, invalid-ID skipping, and all 256 E4M3 codes against
 ``torch.float8_e4m3fn``. The expert-range form (only experts [expert_base,
 expert_base + E) held here) is pinned by hand-worked range fixtures, the
 sort-based brute force with a range, disjoint shards partitioning the routes,
-the loop FFN with a range, and shard outputs summing to the full layer. Every function below is pinned by at least one of
-these; none is "parity unpinned".
+the loop FFN with a range, and shard outputs summing to the full layer.
+Every function below is pinned by at least one of these; none is "parity
+unpinned".
 """
 from .moe_oracle import (  # noqa: F401
     align,

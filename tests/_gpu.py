@@ -77,3 +77,21 @@ def run_align(ids_np, E, b, capacity=None):
     moe.moe_align(ids, E, b, s, blocks, n)
     torch.cuda.synchronize()
     return s.cpu().numpy(), blocks.cpu().numpy(), int(n.cpu().numpy()[0])
+
+
+def run_align_ex(ids_np, E, expert_base, b, use_ws=True, capacity=None):
+    """moe_align_ex with (use_ws) or without the multi-workgroup workspace."""
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(DEV)
+    M, k = ids_np.shape
+    cap = moe.moe_align_capacity(M, k, E, b) if capacity is None else capacity
+    s = torch.full((max(cap, 1),), POISON, dtype=torch.int32, device=DEV)[:cap]
+    blocks = torch.full((max(cap // b, 1),), POISON, dtype=torch.int32, device=DEV)[:cap // b]
+    n = torch.full((1,), POISON, dtype=torch.int32, device=DEV)
+    ws = None
+    if use_ws:
+        nbytes = moe.moe_align_ex_workspace_size(M, k, E)
+        if nbytes:
+            ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device=DEV)
+    moe.moe_align_ex(ids, E, expert_base, b, s, blocks, n, ws=ws)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), blocks.cpu().numpy(), int(n.cpu().numpy()[0])

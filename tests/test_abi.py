@@ -58,12 +58,33 @@ def test_align_validation():
     assert L.moe_status_str(B.MOE_ERR_CAPACITY) == b"alignment capacity too small"
 
 
+def test_align_ex_workspace_and_validation():
+    L = moe.lib()
+    assert moe.moe_align_ex_workspace_size(1024, 8, 128) == 0          # 8192 routes: one workgroup
+    n = moe.moe_align_ex_workspace_size(1025, 8, 128)                  # 8200 routes: 3 workgroups
+    assert n >= (3 * 128 + 128) * 4 and n % 256 == 0
+    assert moe.moe_align_ex_workspace_size(2**21, 8, 2048) >= (4096 * 2048 + 2048) * 4
+    size = ctypes.c_size_t(0)
+    assert L.moe_align_ex_workspace_size(4, 0, 8, ctypes.byref(size)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_align_ex_workspace_size(4, 2, 4096, ctypes.byref(size)) == B.MOE_ERR_UNSUPPORTED
+    cap = moe.moe_align_capacity(4096, 8, 16, 8)
+    ex = L.moe_align_ex
+    assert ex(FAKE, 4, 2, 8, -1, 8, FAKE, FAKE, FAKE, 64, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert ex(FAKE, 4, 2, 8, 2**31 - 4, 8, FAKE, FAKE, FAKE, 64, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert ex(FAKE, 4096, 8, 16, 32, 8, FAKE, FAKE, FAKE, cap - 8, None, 0, None) == B.MOE_ERR_CAPACITY
+    need = moe.moe_align_ex_workspace_size(4096, 8, 16)
+    assert need > 0
+    assert ex(FAKE, 4096, 8, 16, 32, 8, FAKE, FAKE, FAKE, cap, FAKE, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert ex(FAKE, 4096, 8, 16, 32, 8, FAKE, FAKE, FAKE, cap, FAKE + 16, need, None) == B.MOE_ERR_INVALID_ARG
+    assert ex(FAKE, 0, 8, 16, 32, 8, None, None, None, 0, None, 0, None) == B.MOE_OK
+
+
 def _w(fmt=B.MOE_W_INT4_AWQ, g=128, q=FAKE, s=FAKE, z=FAKE):
     return B.moe_weights(fmt, g, q, s, z)
 
 
-def _desc(M=1, H=2048, I=768, E=128, k=8, b=8, path=B.MOE_PATH_AUTO, g13=128, g2=128, **kw):
-    return B.make_desc(M, H, I, E, k, b, _w(g=g13, **kw), _w(g=g2, **kw), path, 0)
+def _desc(M=1, H=2048, I=768, E=128, k=8, b=8, path=B.MOE_PATH_AUTO, g13=128, g2=128, expert_base=0, **kw):
+    return B.make_desc(M, H, I, E, k, b, _w(g=g13, **kw), _w(g=g2, **kw), path, 0, expert_base)
 
 
 def _ws_status(d):
@@ -100,7 +121,11 @@ def test_auto_path_threshold():
 def test_desc_validation():
     assert _ws_status(_desc(M=-1)) == B.MOE_ERR_INVALID_ARG
     assert _ws_status(_desc(k=0)) == B.MOE_ERR_INVALID_ARG
-    assert _ws_status(_desc(k=200)) == B.MOE_ERR_INVALID_ARG       # k > E
+    assert _ws_status(_desc(k=200)) == B.MOE_ERR_UNSUPPORTED       # decode: at most 16 routes per token
+    assert _ws_status(_desc(M=64, E=4, k=8)) == B.MOE_OK            # a shard may hold fewer experts than k
+    assert _ws_status(_desc(expert_base=-1)) == B.MOE_ERR_INVALID_ARG
+    assert _ws_status(_desc(expert_base=2**31 - 100)) == B.MOE_ERR_INVALID_ARG   # base + E overflows
+    assert _ws_status(_desc(expert_base=2**31 - 129)) == B.MOE_OK
     assert _ws_status(_desc(b=0)) == B.MOE_ERR_INVALID_ARG
     assert _ws_status(_desc(H=2000)) == B.MOE_ERR_INVALID_ARG      # not a multiple of 32
     assert _ws_status(_desc(g13=96)) == B.MOE_ERR_INVALID_ARG      # H % g != 0
