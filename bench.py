@@ -93,6 +93,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 64 MiB device copy (the counter calibration kernel) and exit")
+    p.add_argument("--grouped-sweep", default=None, metavar="FMT",
+                   help="only run the grouped-GEMM shape sweep on the batched layout (int4 or mxfp8) and exit")
     return p.parse_args()
 
 
@@ -276,6 +278,89 @@ def layer_numbers(rot, steps):
     }
 
 
+SWEEP_G = (8, 16, 32, 64, 128)
+SWEEP_N = (16, 32, 64, 128, 256, 512, 1024)
+SWEEP_COLD_BYTES = 640 << 20    # weight copies rotated per point: more than the 256 MB Infinity Cache
+
+
+def grouped_sweep(fmt):
+    """The two grouped GEMMs of a Qwen3-30B-A3B-shaped layer (gate/up: 1536 x
+    2048, down: 2048 x 768; H = 2048, I = 768) on the fixed-capacity batched
+    layout, over G experts and a maximum of N tokens per expert with the
+    ragged counts {N, 3N/4, N/2, N/4} repeated over the experts. Median
+    graph-replay latency per call over cold weight copies; TFLOP/s_eff counts
+    2 M K sum(N_g) (unpadded); weight GB/s counts the G experts' packed bytes."""
+    import dataclasses
+    import statistics
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    from workloads import CONFIGS, make_weights
+    base = CONFIGS["mxfp8_m64" if fmt == "mxfp8" else "batch_m256_zipf"]
+    cfg = dataclasses.replace(base, E=max(SWEEP_G), b=64)
+    w13, w2 = make_weights(cfg, 0, 0)
+    H, I = cfg.H, cfg.I
+    full13 = moe.DeviceProjection.from_host(w13, "cuda")
+    full2 = moe.DeviceProjection.from_host(w2, "cuda")
+    per13 = full13.nbytes() / cfg.E
+    per2 = full2.nbytes() / cfg.E
+    rng = np.random.default_rng(0)
+    rows = []
+    for G in SWEEP_G:
+        def take(p):
+            return moe.DeviceProjection(p.fmt, p.group, p.q[:G].clone(), p.scale[:G].clone(),
+                                        None if p.zero is None else p.zero[:G].clone())
+        copies = max(2, int(math.ceil(SWEEP_COLD_BYTES / (G * (per13 + per2)))))
+        layers = [moe.MoeLayer(take(full13), take(full2), G, H, I, 1, 64) for _ in range(copies)]
+        for N in SWEEP_N:
+            counts_l = [[N, 3 * N // 4, N // 2, N // 4][e % 4] for e in range(G)]
+            counts = torch.tensor(counts_l, dtype=torch.int32, device="cuda")
+            xv = rng.standard_normal((G, N, H)).astype(np.float32)
+            xb = torch.from_numpy((xv.view(np.uint32) >> 16).astype(np.uint16).view(np.int16)).cuda() \
+                .view(torch.bfloat16)
+            hi = torch.zeros((G, N, I), dtype=torch.bfloat16, device="cuda")
+            lo = torch.zeros_like(hi)
+            yb = torch.zeros((G, N, H), dtype=torch.float32, device="cuda")
+            descs = [L.desc(1) for L in layers]
+            stages = {
+                "gate_up": (lambda d: moe.moe_ffn_gate_up_batched(d, xb, counts, hi, lo), 2 * I, H, per13),
+                "down": (lambda d: moe.moe_ffn_down_batched(d, hi, lo, counts, yb), H, I, per2),
+            }
+            for name, (fn, Mdim, Kdim, per) in stages.items():
+                stream = torch.cuda.Stream()
+                with torch.cuda.stream(stream):
+                    for d in descs[:2]:
+                        fn(d)
+                torch.cuda.synchronize()
+                reps = max(copies, 16)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(reps):
+                        fn(descs[i % copies])
+                g.replay()
+                torch.cuda.synchronize()
+                times = []
+                for _ in range(5):
+                    t0 = torch.cuda.Event(enable_timing=True)
+                    t1 = torch.cuda.Event(enable_timing=True)
+                    t0.record()
+                    g.replay()
+                    t1.record()
+                    torch.cuda.synchronize()
+                    times.append(t0.elapsed_time(t1) * 1e3 / reps)
+                us = statistics.median(times)
+                flops = 2.0 * Mdim * Kdim * sum(counts_l)
+                rows.append({"layer": name, "G": G, "N": N, "us": round(us, 2),
+                             "tflops_eff": round(flops / (us * 1e-6) / 1e12, 2),
+                             "weight_GBps": round(G * per / (us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(G * per / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+                log(json.dumps(rows[-1]))
+            del xb, hi, lo, yb
+        del layers
+        torch.cuda.empty_cache()
+    print(json.dumps({"grouped_sweep": fmt, "shapes": "Qwen3-30B-A3B H=2048 I=768", "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -287,6 +372,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.grouped_sweep:
+        grouped_sweep(args.grouped_sweep)
         return
     import mixture_experts_ffn_align_amd as moe
     moe.lib()  # fail loudly if the HIP library is missing

@@ -205,6 +205,32 @@ MOE_API moe_status moe_ffn_down_combine(const moe_ffn_desc* d, const int32_t* to
                                         const float* topk_w, float* y, void* ws, size_t ws_bytes,
                                         hipStream_t stream);
 
+/* The grouped path's two GEMMs on a fixed-capacity batched layout (the
+ * layout of "Hardware-Native Joint Sparse-Quantization for Trillion-Scale
+ * MoE", App. D.1: every expert's operands at a fixed stride, token counts
+ * kept on the device, a partial last tile per expert). Expert e (weight index
+ * e, 0 <= e < E) owns rows e*capacity .. e*capacity + counts[e] - 1 of every
+ * batched operand; counts[e] is read on the device and clamped to
+ * [0, capacity]; rows past it are neither read nor written.
+ *   xb        bf16 [E][capacity][H]            (gate/up input)
+ *   a_hi/a_lo bf16 [E][capacity][I] planes of silu(gate)*up = hi + lo
+ *             (gate/up output, down input; the layout of moe_ffn_intermediate)
+ *   yb        fp32 [E][capacity][H]            (down output, before any combine)
+ *   counts    int32 [E] device
+ * Uses d->H, I, E, b (rows per tile, <= 64), w13 / w2 and max_workgroups; M, k,
+ * path and expert_base are not used. Same arithmetic, per row, as the grouped
+ * path of moe_ffn_forward.
+ * Errors: MOE_ERR_INVALID_ARG (null or misaligned pointers: 16 bytes for the
+ * row arrays; capacity < 1; the layer checks of moe_ffn_forward),
+ * MOE_ERR_UNSUPPORTED (grouped-path shape rules; E*capacity > INT32_MAX),
+ * MOE_ERR_HIP. */
+MOE_API moe_status moe_ffn_gate_up_batched(const moe_ffn_desc* d, const uint16_t* xb, const int32_t* counts,
+                                           int32_t capacity, uint16_t* a_hi, uint16_t* a_lo,
+                                           hipStream_t stream);
+MOE_API moe_status moe_ffn_down_batched(const moe_ffn_desc* d, const uint16_t* a_hi, const uint16_t* a_lo,
+                                        const int32_t* counts, int32_t capacity, float* yb,
+                                        hipStream_t stream);
+
 /* Number of kernels moe_ffn_forward launches for this description (0 on error). */
 MOE_API int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
 

@@ -70,6 +70,10 @@ _SIGNATURES = {
                                  _c_ptr]),
     "moe_ffn_down_combine": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                       _c_size, _c_ptr]),
+    "moe_ffn_gate_up_batched": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_i32, _c_ptr,
+                                         _c_ptr, _c_ptr]),
+    "moe_ffn_down_batched": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_i32,
+                                      _c_ptr, _c_ptr]),
     "moe_ffn_kernel_count": (_c_i32, [ctypes.POINTER(moe_ffn_desc)]),
     "moe_ffn_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(moe_ffn_desc), _c_i32]),
     "moe_ffn_intermediate": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size),
@@ -226,6 +230,20 @@ def moe_ffn_down_combine(desc: moe_ffn_desc, topk_ids, topk_w, y, ws, stream=Non
     _check(lib().moe_ffn_down_combine(ctypes.byref(desc), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_ffn_down_combine")
+
+
+def moe_ffn_gate_up_batched(desc: moe_ffn_desc, xb, counts, a_hi, a_lo, stream=None) -> None:
+    """xb [E, capacity, H] bf16, counts [E] int32 (device), a_hi / a_lo [E, capacity, I]."""
+    _check(lib().moe_ffn_gate_up_batched(ctypes.byref(desc), _ptr(xb), _ptr(counts), xb.shape[1],
+                                         _ptr(a_hi), _ptr(a_lo), _stream(stream)),
+           "moe_ffn_gate_up_batched")
+
+
+def moe_ffn_down_batched(desc: moe_ffn_desc, a_hi, a_lo, counts, yb, stream=None) -> None:
+    """a_hi / a_lo [E, capacity, I] bf16 planes, counts [E] int32, yb [E, capacity, H] fp32."""
+    _check(lib().moe_ffn_down_batched(ctypes.byref(desc), _ptr(a_hi), _ptr(a_lo), _ptr(counts),
+                                      a_hi.shape[1], _ptr(yb), _stream(stream)),
+           "moe_ffn_down_batched")
 
 
 def moe_ffn_kernel_count(desc: moe_ffn_desc) -> int:

@@ -312,6 +312,68 @@ moe_status moe_ffn_down_combine(const moe_ffn_desc* d, const int32_t* topk_ids, 
                      stream, nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation of the batched-layout GEMM calls: the layer shape and weights
+// as for moe_ffn_forward (M, k, path and expert_base are not used), the
+// grouped path's shape rules, and a capacity whose row indices fit int32.
+moe_status validate_batched(const moe_ffn_desc* d, int32_t capacity) {
+  if (d == nullptr || capacity < 1) return MOE_ERR_INVALID_ARG;
+  moe_ffn_desc t = *d;
+  t.M = 1;
+  t.k = 1;
+  t.path = MOE_PATH_GROUPED;
+  t.expert_base = 0;
+  Layout L;
+  const moe_status st = validate(&t, &L, true);
+  if (st != MOE_OK) return st;
+  if (int64_t(d->E) * capacity > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe::GroupedArgs batched_args(const moe_ffn_desc* d) {
+  moe::GroupedArgs p{};
+  p.w13 = d->w13;
+  p.w2 = d->w2;
+  p.H = d->H; p.I = d->I; p.E = d->E; p.b = d->b;
+  p.max_workgroups = d->max_workgroups;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_ffn_gate_up_batched(const moe_ffn_desc* d, const uint16_t* xb, const int32_t* counts,
+                                   int32_t capacity, uint16_t* a_hi, uint16_t* a_lo, hipStream_t stream) {
+  moe_status st = validate_batched(d, capacity);
+  if (st != MOE_OK) return st;
+  if (xb == nullptr || counts == nullptr || a_hi == nullptr || a_lo == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(xb, 16) || !aligned(a_hi, 16) || !aligned(a_lo, 16) || !aligned(counts, 4))
+    return MOE_ERR_INVALID_ARG;
+  moe::GroupedArgs p = batched_args(d);
+  p.x = xb;
+  p.a_hi = a_hi;
+  p.a_lo = a_lo;
+  return hip_status(moe::launch_grouped_gate_up_batched(p, counts, capacity, stream));
+}
+
+moe_status moe_ffn_down_batched(const moe_ffn_desc* d, const uint16_t* a_hi, const uint16_t* a_lo,
+                                const int32_t* counts, int32_t capacity, float* yb, hipStream_t stream) {
+  moe_status st = validate_batched(d, capacity);
+  if (st != MOE_OK) return st;
+  if (a_hi == nullptr || a_lo == nullptr || counts == nullptr || yb == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(a_hi, 16) || !aligned(a_lo, 16) || !aligned(yb, 16) || !aligned(counts, 4))
+    return MOE_ERR_INVALID_ARG;
+  moe::GroupedArgs p = batched_args(d);
+  p.a_hi = const_cast<uint16_t*>(a_hi);   // read only: the down GEMM's input planes
+  p.a_lo = const_cast<uint16_t*>(a_lo);
+  p.yhat = yb;
+  return hip_status(moe::launch_grouped_down_batched(p, counts, capacity, stream));
+}
+
 int32_t moe_ffn_kernel_count(const moe_ffn_desc* d) {
   Layout L;
   if (validate(d, &L, false) != MOE_OK) return 0;

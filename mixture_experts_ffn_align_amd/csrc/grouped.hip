@@ -119,9 +119,12 @@ __device__ __forceinline__ void wait_vm_le(int n) {
 struct GemmParams {
   const uint16_t* b0;            // B rows (bf16, K per row): x [M] or a_hi [Mk]
   const uint16_t* b1;            // second plane (a_lo) or null
-  const int32_t* sorted;
+  const int32_t* sorted;         // aligned rows (null in the batched layout)
   const int32_t* blocks;
   const int32_t* num_padded;
+  const int32_t* counts;         // batched layout: rows of each expert [E], else null
+  int cap;                       // batched layout: rows reserved per expert
+  int nbpe;                      // batched layout: blocks per expert, ceil(cap / b)
   const unsigned char* q;        // int4: u32 [E][rows][K/8]; MXFP8: E4M3 [E][rows][K]
   const unsigned char* sc;       // int4: fp16 [E][rows][K/g]; MXFP8: E8M0 [E][rows][K/32]
   const uint8_t* zp;
@@ -155,7 +158,6 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
   constexpr int kSlabK = 32 * kSteps;                  // reduction elements per slab
   constexpr int kRowBytes = kMx ? kSlabK : kSlabK / 2; // weight bytes per row and slab
   constexpr int kRowsPerDma = 1024 / kRowBytes;        // weight rows per 1 KB LDS-DMA
-  constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row and slab
   constexpr int kABytes = 2 * kTileRows * kRowBytes;   // weight bytes per slab (128 rows)
   constexpr int kScStride = kTileRows * kMaxGpr * 2;   // bytes per row set (fp16 scales)
   constexpr int kZpStride = kTileRows * kMaxGpr;       // bytes per row set (u8 zeros)
@@ -173,7 +175,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
   const int rl = 16 * (wave & 3);                   // first row of this wave within the set
   const int n = lane & 15, lq = lane >> 4;
   const int ntasks = p.nblk * p.ntile;
-  const int npad = p.num_padded[0];
+  const bool batched = p.counts != nullptr;
+  const int npad = batched ? 0 : p.num_padded[0];
   const int row_bytes = kMx ? p.K : p.K / 2, gpr = p.K / p.g;
   constexpr int kScBytes = kMx ? 1 : 2;                 // E8M0 byte or fp16 scale
   const int nslab = p.K / kSlabK;
@@ -182,19 +185,33 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
     const int blk = task / p.ntile;
     const int ng = task - blk * p.ntile;
-    if (blk * p.b >= npad) continue;
-    const int e = p.blocks[blk];
-    if (e < 0 || e >= p.E) continue;
+    int e, nrows;    // the block's expert and, in the batched layout, its valid rows
+    if (batched) {
+      // Block j of expert e covers rows e * cap + j * b .. +b-1 of the batched
+      // operands; rows at or past the expert's count are padding.
+      e = blk / p.nbpe;
+      const int j = blk - e * p.nbpe;
+      const int cnt = min(max(p.counts[e], 0), p.cap);
+      if (j * p.b >= cnt) continue;
+      nrows = min(p.b, cnt - j * p.b);
+    } else {
+      if (blk * p.b >= npad) continue;
+      e = p.blocks[blk];
+      if (e < 0 || e >= p.E) continue;
+      nrows = p.b;
+    }
 
     if (threadIdx.x < kMaxTok) {
       const int c = threadIdx.x;
       int r = -1;
-      if (c < p.b) {
+      if (batched) {
+        if (c < nrows) r = (blk / p.nbpe) * p.cap + (blk % p.nbpe) * p.b + c;
+      } else if (c < p.b) {
         r = p.sorted[static_cast<size_t>(blk) * p.b + c];
         if (r < 0 || r >= p.mk) r = -1;
       }
       cols[c] = r;
-      brow[c] = r < 0 ? 0 : (kGateUp ? r / p.k : r);
+      brow[c] = r < 0 ? 0 : ((kGateUp && !batched) ? r / p.k : r);
     }
     __syncthreads();
     // Active sub-tiles (wave-uniform), listed in order; static indices only,
@@ -590,6 +607,60 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.K = p.I;
   gp.g = p.w2.group;
   const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
+  return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
+}
+
+hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream) {
+  GemmParams gp{};
+  gp.b0 = p.x;
+  gp.counts = counts;
+  gp.cap = cap;
+  gp.nbpe = (cap + p.b - 1) / p.b;
+  gp.q = static_cast<const unsigned char*>(p.w13.q);
+  gp.sc = static_cast<const unsigned char*>(p.w13.scale);
+  gp.zp = p.w13.zero;
+  gp.a_hi = p.a_hi;
+  gp.a_lo = p.a_lo;
+  gp.mk = p.E * cap;
+  gp.k = 1;
+  gp.E = p.E;
+  gp.b = p.b;
+  gp.nblk = p.E * gp.nbpe;
+  gp.ntile = p.I / kTileRows;
+  gp.rows_per_expert = 2 * p.I;
+  gp.set_stride = p.I;
+  gp.tile_stride = kTileRows;
+  gp.out_rows = p.I;
+  gp.K = p.H;
+  gp.g = p.w13.group;
+  const int wgs = grid_for(gp.nblk * gp.ntile, p.max_workgroups);
+  return launch_gemm<true, 1, kGateUpSteps>(p.w13.fmt, gp, wgs, stream);
+}
+
+hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream) {
+  GemmParams gp{};
+  gp.b0 = p.a_hi;
+  gp.b1 = p.a_lo;
+  gp.counts = counts;
+  gp.cap = cap;
+  gp.nbpe = (cap + p.b - 1) / p.b;
+  gp.q = static_cast<const unsigned char*>(p.w2.q);
+  gp.sc = static_cast<const unsigned char*>(p.w2.scale);
+  gp.zp = p.w2.zero;
+  gp.yhat = p.yhat;
+  gp.mk = p.E * cap;
+  gp.k = 1;
+  gp.E = p.E;
+  gp.b = p.b;
+  gp.nblk = p.E * gp.nbpe;
+  gp.ntile = p.H / (2 * kTileRows);
+  gp.rows_per_expert = p.H;
+  gp.set_stride = kTileRows;
+  gp.tile_stride = 2 * kTileRows;
+  gp.out_rows = p.H;
+  gp.K = p.I;
+  gp.g = p.w2.group;
+  const int wgs = grid_for(gp.nblk * gp.ntile, p.max_workgroups);
   return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
 }
 

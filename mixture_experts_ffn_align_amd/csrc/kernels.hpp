@@ -59,5 +59,12 @@ bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2);
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream);
+// The two grouped GEMMs on the fixed-capacity batched layout: expert e's rows
+// are e * cap .. e * cap + counts[e] - 1 of x / the intermediate planes / yhat
+// (counts on the device, clamped to [0, cap]); rows past the count are not
+// read or written. Uses x, w13, w2, a_hi, a_lo, yhat, H, I, E, b and
+// max_workgroups of p.
+hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream);
+hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream);
 
 }  // namespace moe

@@ -26,13 +26,18 @@ W2 scale doubling, invalid-ID skipping, and all 256 E4M3 codes against
 ``torch.float8_e4m3fn``. The expert-range form (only experts [expert_base,
 expert_base + E) held here) is pinned by hand-worked range fixtures, the
 sort-based brute force with a range, disjoint shards partitioning the routes,
-the loop FFN with a range, and shard outputs summing to the full layer.
+the loop FFN with a range, and shard outputs summing to the full layer. The
+batched-layout GEMMs are pinned by a loop over elements on tiny shapes and
+by the routed layer's own per-route surfaces when the batch is built from a
+routing.
 Every function below is pinned by at least one of these; none is "parity
 unpinned".
 """
 from .moe_oracle import (  # noqa: F401
     align,
     align_capacity,
+    batched_down,
+    batched_gate_up,
     bf16_to_f64,
     dequant_int4,
     dequant_mxfp8,

@@ -235,3 +235,47 @@ def ffn_stages(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
 def ffn(x_bits, topk_ids, topk_w, w13, w2, E: int, expert_base: int = 0) -> np.ndarray:
     """Layer output y [M, H] in float64 (see ``ffn_stages``)."""
     return ffn_stages(x_bits, topk_ids, topk_w, w13, w2, E, expert_base)["y"]
+
+
+# ----------------------------------------------------------------------------
+# 5. The two grouped GEMMs on a fixed-capacity batched layout  [P2, App. D.1:
+#    operands of expert e at a fixed stride with a per-expert capacity, token
+#    counts kept on the device; the GEMM shapes of App. D.2, Table 8]
+# ----------------------------------------------------------------------------
+
+def _valid_rows(counts, cap: int) -> np.ndarray:
+    return np.clip(np.asarray(counts, dtype=np.int64), 0, cap)
+
+
+def batched_gate_up(xb_bits: np.ndarray, counts: np.ndarray, w13) -> np.ndarray:
+    """a [E, cap, I] float64: for expert e and row n < clamp(counts[e], 0, cap),
+    a[e, n] = silu(W13[e, 0:I] x[e, n]) * (W13[e, I:2I] x[e, n]) with x the
+    bf16 rows of ``xb_bits`` [E, cap, H] (the gate/up expert product of
+    ``ffn_stages``); rows at or past the count are zero."""
+    x = bf16_to_f64(xb_bits)
+    E, cap, H = x.shape
+    I = w13.N // 2
+    n = _valid_rows(counts, cap)
+    a = np.zeros((E, cap, I))
+    for e in range(E):
+        if n[e] == 0:
+            continue
+        W13 = _dequant(w13, e)
+        X = x[e, :n[e]]
+        a[e, :n[e]] = _silu(X @ W13[:I].T) * (X @ W13[I:].T)
+    return a
+
+
+def batched_down(a: np.ndarray, counts: np.ndarray, w2) -> np.ndarray:
+    """yhat [E, cap, H] float64: yhat[e, n] = W2[e] a[e, n] for n <
+    clamp(counts[e], 0, cap) (the down expert product of ``ffn_stages``,
+    before any combine); rows at or past the count are zero."""
+    E, cap, _ = a.shape
+    H = w2.N
+    n = _valid_rows(counts, cap)
+    y = np.zeros((E, cap, H))
+    for e in range(E):
+        if n[e] == 0:
+            continue
+        y[e, :n[e]] = a[e, :n[e]] @ _dequant(w2, e).T
+    return y

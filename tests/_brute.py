@@ -77,3 +77,25 @@ def brute_ffn(x_bits, topk_ids, topk_w, w13, w2, E, base=0):
                     acc += a[i] * deq_elem(q2, s2, z2, g2, e, h, i)
                 y[t][h] += wt * acc
     return y
+
+
+def brute_batched(x_bits, counts, w13, w2):
+    """Per expert e and row n < clamp(counts[e]): the gate/up product a and the
+    down product yhat by explicit loops (lists of lists)."""
+    E, cap, H = len(x_bits), len(x_bits[0]), len(x_bits[0][0])
+    I = w13.N // 2
+    q13, s13, z13, g13 = w13.q.tolist(), w13.s.astype(float).tolist(), w13.z.tolist(), w13.g
+    q2, s2, z2, g2 = w2.q.tolist(), w2.s.astype(float).tolist(), w2.z.tolist(), w2.g
+    a = [[[0.0] * I for _ in range(cap)] for _ in range(E)]
+    y = [[[0.0] * H for _ in range(cap)] for _ in range(E)]
+    for e in range(E):
+        n_e = min(max(int(counts[e]), 0), cap)
+        for n in range(n_e):
+            x = [bf16_bits_to_float(v) for v in x_bits[e][n]]
+            for i in range(I):
+                gate = sum(x[h] * deq_elem(q13, s13, z13, g13, e, i, h) for h in range(H))
+                up = sum(x[h] * deq_elem(q13, s13, z13, g13, e, I + i, h) for h in range(H))
+                a[e][n][i] = gate / (1.0 + math.exp(-gate)) * up
+            for h in range(H):
+                y[e][n][h] = sum(a[e][n][i] * deq_elem(q2, s2, z2, g2, e, h, i) for i in range(I))
+    return a, y

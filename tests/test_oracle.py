@@ -295,6 +295,46 @@ def test_ffn_expert_shards_sum_to_the_full_layer():
     np.testing.assert_allclose(parts, full, rtol=1e-12, atol=1e-12 * np.abs(full).max())
 
 
+def test_batched_gemms_match_loop_brute_force():
+    cfg = _tiny_cfg(M=2, H=64, I=32, E=3, k=1, g=32)
+    wl = make_workload(cfg, seed=6)
+    rng = np.random.default_rng(6)
+    cap = 3
+    xb = rng.integers(0, 2**16, size=(3, cap, 64)).astype(np.uint16)
+    xb = ((xb & 0x807F) | 0x3F00).astype(np.uint16)    # bf16 values in [-2, 2)
+    counts = np.array([2, 0, 7], dtype=np.int32)       # 7 > cap is clamped
+    a = oracle.batched_gate_up(xb, counts, wl.w13)
+    y = oracle.batched_down(a, counts, wl.w2)
+    ab, yb = _brute.brute_batched(xb.tolist(), counts, wl.w13, wl.w2)
+    np.testing.assert_allclose(a, np.array(ab), rtol=1e-12, atol=1e-12 * np.abs(ab).max())
+    np.testing.assert_allclose(y, np.array(yb), rtol=1e-12, atol=1e-12 * np.abs(yb).max())
+    assert not a[1].any() and not a[0, 2].any()
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS["tiny"], _tiny_cfg(M=40, H=256, I=128, E=16, k=4, g=64)],
+                         ids=["tiny", "m40_e16"])
+def test_batched_gemms_equal_routed_layer_surfaces(cfg):
+    # Gather each expert's routes into its batch rows (route order): the
+    # batched products are the routed layer's a and yhat rows.
+    wl = make_workload(cfg, seed=2)
+    E, k = wl.cfg.E, wl.cfg.k
+    flat = wl.topk_ids.reshape(-1)
+    counts = np.array([(flat == e).sum() for e in range(E)], dtype=np.int32)
+    cap = max(1, int(counts.max()))
+    xb = np.zeros((E, cap, wl.cfg.H), dtype=np.uint16)
+    where = {}
+    for e in range(E):
+        for n, r in enumerate(np.nonzero(flat == e)[0]):
+            xb[e, n] = wl.x[r // k]
+            where[r] = (e, n)
+    st = oracle.ffn_stages(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, E)
+    a = oracle.batched_gate_up(xb, counts, wl.w13)
+    y = oracle.batched_down(a, counts, wl.w2)
+    for r, (e, n) in where.items():
+        np.testing.assert_allclose(a[e, n], st["a"][r], rtol=1e-12, atol=1e-12 * np.abs(st["a"]).max())
+        np.testing.assert_allclose(y[e, n], st["yhat"][r], rtol=1e-12, atol=1e-12 * np.abs(st["yhat"]).max())
+
+
 def _identical_experts(wl):
     """Copy expert 0's packed weights into every expert."""
     def rep(pw):
