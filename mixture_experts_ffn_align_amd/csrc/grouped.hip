@@ -418,6 +418,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(cs[i], d[i], acc[u][i]);
+          // Keep this sub-tile's accumulation in its own iteration: the
+          // compiler can otherwise merge the accumulations into one tail that
+          // the loop exit jumps into right after an MFMA whose result it
+          // reads, without the wait states that read needs (seen on gfx950
+          // with ROCm 7.2: wrong sums for the last of two or three sub-tiles).
+          asm volatile("" : "+v"(acc[u]));
         }
       }
       if (++gcount == spg) {

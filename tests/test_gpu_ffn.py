@@ -67,6 +67,11 @@ RAGGED = [
     dict(M=2, H=256, I=1536, E=16, k=12, b=8, g=128),
     # A group spanning two 128-element slabs.
     dict(M=6, H=512, I=256, E=8, k=2, b=16, g=256),
+    # Groups shorter than a slab with full 64-column blocks (several scaled
+    # partials per slab on four sub-tiles).
+    dict(M=200, H=256, I=128, E=4, k=2, b=64, g=64),
+    dict(M=150, H=512, I=256, E=4, k=2, b=64, g=32),
+    dict(M=120, H=256, I=128, E=4, k=2, b=32, g=64),
     # MXFP8 weights (E4M3 + E8M0 per 32): several lane layouts, k > 8, full blocks.
     dict(M=5, H=256, I=128, E=8, k=2, b=8, g=32, fmt="mxfp8"),
     dict(M=3, H=512, I=448, E=16, k=5, b=8, g=32, fmt="mxfp8"),
