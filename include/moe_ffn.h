@@ -68,7 +68,8 @@ typedef enum {
 } moe_wfmt;
 
 typedef enum {
-  MOE_PATH_AUTO = 0,     /* decode for M <= moe_ffn_auto_decode_max_m(), else grouped */
+  MOE_PATH_AUTO = 0,     /* decode for M <= moe_ffn_auto_decode_max_m(), else grouped; when the
+                            decode path's shape rules fail, grouped */
   MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
   MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised bf16 MFMA grouped GEMMs + combine */
 } moe_path;
@@ -90,7 +91,8 @@ typedef struct {
   int32_t I;               /* per-expert intermediate size, multiple of 32 and of w2.group */
   int32_t E;               /* experts held here (1..2048): IDs expert_base .. expert_base + E - 1 */
   int32_t k;               /* routes per token (>= 1) */
-  int32_t b;               /* alignment block size used by the grouped path (>= 1) */
+  int32_t b;               /* alignment block size used by the grouped path (>= 1; the
+                              grouped GEMMs take b <= 64) */
   moe_weights w13;
   moe_weights w2;
   int32_t path;            /* moe_path */
@@ -162,7 +164,9 @@ MOE_API moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes);
  * warp-decode write-up, "Eliminación del relleno"); the grouped path runs
  * moe_align into the workspace first. The route-indexed intermediate
  * silu(gate)*up is left in the workspace (see moe_ffn_intermediate).
- * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED (the path's shape rules, or
+ * a layer whose kernels would have more than 2^30 tasks), MOE_ERR_WORKSPACE,
+ * MOE_ERR_HIP. */
 MOE_API moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
                            const float* topk_w, float* y, void* ws, size_t ws_bytes,
                            hipStream_t stream);
@@ -247,6 +251,10 @@ MOE_API moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, s
 
 /* Largest M for which MOE_PATH_AUTO picks the decode path. */
 MOE_API int32_t moe_ffn_auto_decode_max_m(void);
+
+/* The path moe_ffn_forward takes for this description (MOE_PATH_AUTO
+ * resolved), or -1 when the description is rejected. Host-only. */
+MOE_API int32_t moe_ffn_resolved_path(const moe_ffn_desc* d);
 
 /* Static string for a status code. */
 MOE_API const char* moe_status_str(moe_status s);

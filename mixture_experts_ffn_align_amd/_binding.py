@@ -79,6 +79,7 @@ _SIGNATURES = {
     "moe_ffn_intermediate": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size),
                                       ctypes.POINTER(_c_size), ctypes.POINTER(_c_i32)]),
     "moe_ffn_auto_decode_max_m": (_c_i32, []),
+    "moe_ffn_resolved_path": (_c_i32, [ctypes.POINTER(moe_ffn_desc)]),
     "moe_status_str": (ctypes.c_char_p, [_c_i32]),
 }
 
@@ -264,3 +265,8 @@ def moe_ffn_intermediate(desc: moe_ffn_desc) -> tuple[int, int, int]:
 
 def moe_ffn_auto_decode_max_m() -> int:
     return int(lib().moe_ffn_auto_decode_max_m())
+
+
+def moe_ffn_resolved_path(desc: moe_ffn_desc) -> int:
+    """The path moe_ffn_forward takes for `desc` (-1 if it is rejected)."""
+    return int(lib().moe_ffn_resolved_path(ctypes.byref(desc)))

@@ -14,6 +14,7 @@ namespace {
 constexpr int32_t kMaxExperts = 2048;
 constexpr int64_t kMaxRoutes = int64_t(1) << 24;
 constexpr int32_t kAutoDecodeMaxM = 16;
+constexpr int64_t kMaxTasks = int64_t(1) << 30;
 
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -40,6 +41,28 @@ bool weights_ok(const moe_weights& w) {
   return true;
 }
 
+// MOE_PATH_AUTO: the decode path for M <= kAutoDecodeMaxM, else the grouped
+// path (the two cross between M = 16 and M = 21 on the Qwen3-30B-A3B-sized
+// layer: expert-centric packing wins once tokens share experts).
+int auto_path(const moe_ffn_desc* d) { return d->M <= kAutoDecodeMaxM ? MOE_PATH_DECODE : MOE_PATH_GROUPED; }
+
+bool shape_ok(int path, const moe_ffn_desc* d) {
+  if (path == MOE_PATH_DECODE)
+    return moe::decode_shape_ok(d->w13.fmt, d->H, d->I, d->k, d->w13.group, d->w2.group);
+  return moe::grouped_shape_ok(d->w13.fmt, d->H, d->I, d->b, d->w13.group, d->w2.group);
+}
+
+// Task counts of the path's kernels (waves or workgroups; the combine's
+// threads) stay below kMaxTasks, so that int32 task indices and the
+// grid-stride steps past the last task do not overflow.
+bool tasks_fit(int path, const moe_ffn_desc* d, int64_t mk) {
+  const int64_t M = d->M, H = d->H, I = d->I;
+  if (path == MOE_PATH_DECODE) return mk * (I / 2) <= kMaxTasks && M * (H / 8) <= kMaxTasks;
+  const int64_t nblk = static_cast<int64_t>(capacity_of(d->M, d->k, d->E, d->b)) / d->b;
+  if (M * (H / 4) > kMaxTasks) return false;
+  return nblk * (I / 64) <= kMaxTasks && nblk * (H / 128) <= kMaxTasks;
+}
+
 moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
   if (d->M < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->k < 1 || d->b < 1) return MOE_ERR_INVALID_ARG;
@@ -58,18 +81,21 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (mk > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
 
   int path = d->path;
-  if (path == MOE_PATH_AUTO) path = d->M <= kAutoDecodeMaxM ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
+  if (path == MOE_PATH_AUTO) {
+    path = auto_path(d);
+    if (!shape_ok(path, d)) path = MOE_PATH_GROUPED;
+  }
   if (need_align_buffers) path = MOE_PATH_GROUPED;
   L->path = path;
+  if (!shape_ok(path, d)) return MOE_ERR_UNSUPPORTED;
+  if (!tasks_fit(path, d, mk)) return MOE_ERR_UNSUPPORTED;
   if (path == MOE_PATH_DECODE) {
-    if (!moe::decode_shape_ok(d->w13.fmt, d->H, d->I, d->k, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
     L->off_a = 0;
     L->off_a_lo = round256(size_t(mk) * d->I * sizeof(uint16_t));
     L->total = L->off_a_lo + round256(size_t(mk) * d->I * sizeof(uint16_t));
     if (L->total == 0) L->total = 256;
     return MOE_OK;
   }
-  if (!moe::grouped_shape_ok(d->w13.fmt, d->H, d->I, d->b, d->w13.group, d->w2.group)) return MOE_ERR_UNSUPPORTED;
   L->cap = capacity_of(d->M, d->k, d->E, d->b);
   size_t o = 0;
   L->off_sorted = o; o += round256(L->cap * sizeof(int32_t));
@@ -330,6 +356,9 @@ moe_status validate_batched(const moe_ffn_desc* d, int32_t capacity) {
   const moe_status st = validate(&t, &L, true);
   if (st != MOE_OK) return st;
   if (int64_t(d->E) * capacity > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // GEMM tasks: E * ceil(capacity / b) blocks times the tiles per block.
+  const int64_t nblk = int64_t(d->E) * ((int64_t(capacity) + d->b - 1) / d->b);
+  if (nblk * (d->I / 64) > kMaxTasks || nblk * (d->H / 128) > kMaxTasks) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -405,6 +434,12 @@ moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* l
 }
 
 int32_t moe_ffn_auto_decode_max_m(void) { return kAutoDecodeMaxM; }
+
+int32_t moe_ffn_resolved_path(const moe_ffn_desc* d) {
+  Layout L;
+  if (validate(d, &L, false) != MOE_OK) return -1;
+  return L.path;
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {

@@ -381,11 +381,6 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
   }
 }
 
-int grid_for(int work_groups, int max_workgroups) {
-  if (work_groups < 1) work_groups = 1;
-  return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : work_groups;
-}
-
 int log2_of(int g) {
   int s = 0;
   while ((1 << s) < g) ++s;
@@ -428,7 +423,7 @@ bool decode_shape_ok(int fmt, int H, int I, int k, int g13, int g2) {
 
 hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const int mk = p.M * p.k;
-  const int waves = mk * (p.I / kNpw);
+  const int64_t waves = int64_t(mk) * (p.I / kNpw);
   const int wgs = grid_for((waves + kGateUpWaves - 1) / kGateUpWaves, p.max_workgroups);
   const auto* q = static_cast<const unsigned char*>(p.w13.q);
   const auto* s = static_cast<const unsigned char*>(p.w13.scale);
@@ -442,7 +437,7 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
 }
 
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream) {
-  const int wgs = grid_for(p.M * (p.H / kDownRows), p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.M) * (p.H / kDownRows), p.max_workgroups);
   if (p.w2.fmt == MOE_W_MXFP8) launch_down_fmt<MOE_W_MXFP8>(p, wgs, stream);
   else launch_down_fmt<MOE_W_INT4_AWQ>(p, wgs, stream);
   return hipGetLastError();

@@ -504,11 +504,6 @@ __global__ __launch_bounds__(kThreads) void combine_topk(
   }
 }
 
-int grid_for(int work_groups, int max_workgroups) {
-  if (work_groups < 1) work_groups = 1;
-  return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : work_groups;
-}
-
 // Steps per scaled partial: g / 32 for g below the slab, else a whole slab
 // (g a multiple of the slab).
 int flush_steps(int g, int steps) { return g >= 32 * steps ? steps : g / 32; }
@@ -585,7 +580,7 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.out_rows = p.I;
   gp.K = p.H;
   gp.g = p.w13.group;
-  const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<true, 1, kGateUpSteps>(p.w13.fmt, gp, wgs, stream);
 }
 
@@ -612,7 +607,7 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.out_rows = p.H;
   gp.K = p.I;
   gp.g = p.w2.group;
-  const int wgs = grid_for(p.nblk * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
 }
 
@@ -639,7 +634,7 @@ hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* c
   gp.out_rows = p.I;
   gp.K = p.H;
   gp.g = p.w13.group;
-  const int wgs = grid_for(gp.nblk * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<true, 1, kGateUpSteps>(p.w13.fmt, gp, wgs, stream);
 }
 
@@ -666,12 +661,12 @@ hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* coun
   gp.out_rows = p.H;
   gp.K = p.I;
   gp.g = p.w2.group;
-  const int wgs = grid_for(gp.nblk * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream) {
-  const int total = p.M * (p.H / 4);
+  const int64_t total = int64_t(p.M) * (p.H / 4);
   const int wgs = grid_for((total + kThreads - 1) / kThreads, p.max_workgroups);
   hipLaunchKernelGGL(combine_topk, dim3(wgs), dim3(kThreads), 0, stream, p.yhat, p.ids, p.topk_w,
                      p.y, p.M, p.k, p.E, p.ebase, p.H);

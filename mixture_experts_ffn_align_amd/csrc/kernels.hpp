@@ -9,6 +9,17 @@
 
 namespace moe {
 
+// Every kernel strides over its tasks, so its grid may be smaller than its
+// task count; launches are capped at kMaxGrid workgroups (and at a caller's
+// max_workgroups > 0), which keeps the work-item count of a dispatch within
+// 32 bits. Task counts themselves are int32 (the C ABI rejects larger layers).
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+inline int grid_for(int64_t work_groups, int max_workgroups) {
+  if (work_groups < 1) work_groups = 1;
+  if (work_groups > kMaxGrid) work_groups = kMaxGrid;
+  return (max_workgroups > 0 && max_workgroups < work_groups) ? max_workgroups : static_cast<int>(work_groups);
+}
+
 // Route alignment (align.hip). Up to kAlignSingleMaxRoutes routes run as one
 // workgroup; more (with a workspace of align_ws_bytes) as three launches over
 // workgroups of kAlignRoutesPerGroup routes. Experts [ebase, ebase + E) are
@@ -59,6 +70,7 @@ bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2);
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream);
+
 // The two grouped GEMMs on the fixed-capacity batched layout: expert e's rows
 // are e * cap .. e * cap + counts[e] - 1 of x / the intermediate planes / yhat
 // (counts on the device, clamped to [0, cap]); rows past the count are not

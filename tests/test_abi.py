@@ -116,12 +116,23 @@ def test_auto_path_threshold():
     assert moe.moe_ffn_kernel_count(_desc(M=m + 1)) == 4
     assert moe.moe_ffn_kernel_count(_desc(M=1, path=B.MOE_PATH_GROUPED)) == 4
     assert moe.moe_ffn_kernel_count(_desc(M=500, path=B.MOE_PATH_DECODE)) == 2
+    rp = moe.moe_ffn_resolved_path
+    assert rp(_desc(M=m)) == B.MOE_PATH_DECODE
+    assert rp(_desc(M=m + 1)) == B.MOE_PATH_GROUPED
+    assert rp(_desc(M=256, b=64)) == B.MOE_PATH_GROUPED
+    assert rp(_desc(M=1, path=B.MOE_PATH_GROUPED)) == B.MOE_PATH_GROUPED
+    # A choice whose shape rules fail falls back to the grouped path.
+    assert rp(_desc(M=1, k=20)) == B.MOE_PATH_GROUPED              # decode: at most 16 routes per token
+    assert rp(_desc(M=1, g13=256, g2=256, I=768, H=2048)) == B.MOE_PATH_DECODE
+    assert rp(_desc(M=1, k=20, path=B.MOE_PATH_DECODE)) == -1
+    assert rp(_desc(M=-1)) == -1
 
 
 def test_desc_validation():
     assert _ws_status(_desc(M=-1)) == B.MOE_ERR_INVALID_ARG
     assert _ws_status(_desc(k=0)) == B.MOE_ERR_INVALID_ARG
-    assert _ws_status(_desc(k=200)) == B.MOE_ERR_UNSUPPORTED       # decode: at most 16 routes per token
+    assert _ws_status(_desc(k=200, path=B.MOE_PATH_DECODE)) == B.MOE_ERR_UNSUPPORTED   # at most 16 routes per token
+    assert _ws_status(_desc(k=200)) == B.MOE_OK                     # automatic path: grouped
     assert _ws_status(_desc(M=64, E=4, k=8)) == B.MOE_OK            # a shard may hold fewer experts than k
     assert _ws_status(_desc(expert_base=-1)) == B.MOE_ERR_INVALID_ARG
     assert _ws_status(_desc(expert_base=2**31 - 100)) == B.MOE_ERR_INVALID_ARG   # base + E overflows
@@ -136,6 +147,11 @@ def test_desc_validation():
     assert _ws_status(_desc(path=7)) == B.MOE_ERR_INVALID_ARG
     assert _ws_status(_desc(E=4096, k=8)) == B.MOE_ERR_UNSUPPORTED
     assert _ws_status(_desc(M=256, b=128, path=B.MOE_PATH_GROUPED)) == B.MOE_ERR_UNSUPPORTED
+    # Layers whose kernels would exceed 2^30 tasks are refused, not truncated.
+    assert _ws_status(_desc(M=2**21, path=B.MOE_PATH_DECODE)) == B.MOE_ERR_UNSUPPORTED
+    assert _ws_status(_desc(M=2**21, H=2**14, I=2**14, g13=512, g2=512, b=1,
+                            path=B.MOE_PATH_GROUPED)) == B.MOE_ERR_UNSUPPORTED   # 2^24 blocks x 256 tiles
+    assert _ws_status(_desc(M=2**21)) == B.MOE_OK                   # automatic: grouped, 25M tasks
     d = _desc()
     d.w2.fmt = B.MOE_W_MXFP8
     assert _ws_status(d) == B.MOE_ERR_INVALID_ARG                 # formats differ
