@@ -480,6 +480,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
   }
 }
 
+// Routes of a token taken per round of the combine: their ids, weights and
+// yhat segments are all loaded before any is used (one memory round trip
+// per round instead of one per route).
+constexpr int kCombineChunk = 8;
+
 __global__ __launch_bounds__(kThreads) void combine_topk(
     const float* __restrict__ yhat, const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, float* __restrict__ y, int M, int k, int E, int ebase, int H) {
@@ -489,16 +494,32 @@ __global__ __launch_bounds__(kThreads) void combine_topk(
     const int t = i / quads;
     const int h = (i - t * quads) << 2;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      const int e = ids[r] - ebase;
-      if (e < 0 || e >= E) continue;
-      const float w = topk_w[r];
-      const float4 v = *reinterpret_cast<const float4*>(yhat + static_cast<size_t>(r) * H + h);
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+    for (int j0 = 0; j0 < k; j0 += kCombineChunk) {
+      // Every route row of yhat exists (it may hold stale values for an
+      // invalid route, which the select below never adds); slots past k
+      // re-read the token's first route.
+      int e[kCombineChunk];
+      float w[kCombineChunk];
+      float4 v[kCombineChunk];
+#pragma unroll
+      for (int c = 0; c < kCombineChunk; ++c) {
+        const int r = t * k + (j0 + c < k ? j0 + c : 0);
+        e[c] = ids[r] - ebase;
+        w[c] = topk_w[r];
+        v[c] = *reinterpret_cast<const float4*>(yhat + static_cast<size_t>(r) * H + h);
+      }
+      // Each product is formed and then kept or dropped by a select (no
+      // branch the loads could be moved into).
+#pragma unroll
+      for (int c = 0; c < kCombineChunk; ++c) {
+        const bool ok = j0 + c < k && e[c] >= 0 && e[c] < E;
+        const float4 n = make_float4(fmaf(w[c], v[c].x, acc.x), fmaf(w[c], v[c].y, acc.y),
+                                     fmaf(w[c], v[c].z, acc.z), fmaf(w[c], v[c].w, acc.w));
+        acc.x = ok ? n.x : acc.x;
+        acc.y = ok ? n.y : acc.y;
+        acc.z = ok ? n.z : acc.z;
+        acc.w = ok ? n.w : acc.w;
+      }
     }
     *reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H + h) = acc;
   }
