@@ -150,3 +150,16 @@ def test_ffn_identical_experts_is_dense_swiglu(path):
     g.announce("ffn-identical", path)
     y = dw.forward(PATHS[path]).cpu().numpy()
     assert ffn_mismatch(y, ref.numpy()) is None
+
+
+def test_auto_path_falls_back_to_grouped():
+    # 20 routes per token: the decode path takes at most 16, so the automatic
+    # path runs the grouped path even at M = 2, and matches the oracle.
+    g = _gpu()
+    wl = _custom(13, M=2, H=256, I=128, E=32, k=20, b=8, g=64)
+    dw = g.DeviceWorkload(wl)
+    assert moe.moe_ffn_resolved_path(dw.layer.desc(2, moe.MOE_PATH_AUTO)) == moe.MOE_PATH_GROUPED
+    ref = oracle.ffn(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
+    g.announce("ffn-auto-fallback")
+    y = dw.forward(moe.MOE_PATH_AUTO).cpu().numpy()
+    assert ffn_mismatch(y, ref) is None, ffn_errors(y, ref)
