@@ -142,7 +142,9 @@ struct GemmParams {
 
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * kWave;
-constexpr int kRingBytes = 64 * 1024;
+constexpr int kRingBytes = 64 * 1024;        // two workgroups per CU
+constexpr int kSmallRingBytes = 36 * 1024;   // int4 with b <= 16 (one sub-tile): three per CU
+constexpr int kSmallRingMxBytes = 40 * 1024; // MXFP8 with b <= 16: three per CU
 constexpr int kMaxDepth = 8;
 
 // One workgroup of eight waves computes a tile of 2 x 64 weight rows against
@@ -151,10 +153,16 @@ constexpr int kMaxDepth = 8;
 // rows 16 (w % 4) .. +15 of it.
 // kGateUp: epilogue silu(gate) * up (else yhat rows). kPlanes: B planes (1: x;
 // 2: the hi and lo planes). kSteps: 32-element MFMA steps per slab (4 or 2).
-// kFlush: steps per scaled partial (g / 32, at most kSteps).
-template <int kFmt, bool kGateUp, int kPlanes, int kSteps, int kFlush>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p) {
+// kFlush: steps per scaled partial (g / 32, at most kSteps). kRing: LDS ring
+// bytes (kRingBytes, or a small ring for blocks of one sub-tile, where the
+// kernel is held to 80 VGPRs so that three workgroups share a CU).
+template <int kFmt, bool kGateUp, int kPlanes, int kSteps, int kFlush, int kRing>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kRing == kRingBytes ? 1 : 6)))
+void grouped_gemm(const GemmParams p) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
+  // Sub-tiles a block can have: four (b <= 64), or one with the small ring
+  // (b <= 16, which the launch guarantees).
+  constexpr int kSub = kRing == kRingBytes ? kMaxSub : 1;
   constexpr int kSlabK = 32 * kSteps;                  // reduction elements per slab
   constexpr int kRowBytes = kMx ? kSlabK : kSlabK / 2; // weight bytes per row and slab
   constexpr int kRowsPerDma = 1024 / kRowBytes;        // weight rows per 1 KB LDS-DMA
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
   constexpr int kZpStride = kTileRows * kMaxGpr;       // bytes per row set (u8 zeros)
   constexpr int kADma = kABytes / 1024;                // weight DMAs per slab
   static_assert(kADma == 4 || kADma == 8 || kADma == 16, "weight DMAs per slab");
-  __shared__ __align__(16) unsigned char ring[kRingBytes];
+  __shared__ __align__(16) unsigned char ring[kRing];
   __shared__ __align__(16) unsigned char ssh[2 * kScStride];
   __shared__ __align__(16) unsigned char szz[2 * kZpStride];
   __shared__ int cols[kMaxTok];    // route of each block column, -1 for padding
@@ -218,15 +226,15 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
     // so the lists stay in registers.
     int amask = 0;
 #pragma unroll
-    for (int st = 0; st < kMaxSub; ++st) {
+    for (int st = 0; st < kSub; ++st) {
       if (__ballot(cols[16 * st + n] >= 0) != 0ull) amask |= 1 << st;
     }
     const int nact = __builtin_popcount(amask);
-    int act[kMaxSub];                    // sub-tile of each active index
+    int act[kSub];                    // sub-tile of each active index
     {
       int m = amask;
 #pragma unroll
-      for (int u = 0; u < kMaxSub; ++u) {
+      for (int u = 0; u < kSub; ++u) {
         act[u] = m ? __builtin_ctz(m) : 0;
         m &= m - 1;
       }
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
     // activations of every (plane, active sub-tile, step), 1 KB each.
     const int nbdma = nact * kPlanes * kSteps;                 // activation DMAs per slab
     const int slot_bytes = kABytes + nbdma * 1024;
-    const int depth_fit = kRingBytes / slot_bytes;
+    const int depth_fit = kRing / slot_bytes;
     const int depth = depth_fit < kMaxDepth ? depth_fit : kMaxDepth;   // >= 2 by construction
     // This wave's DMAs per slab: weight DMA i goes to wave i, activation DMA
     // i to wave i % 8.
@@ -322,9 +330,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
       bnext1 += kSlabK;
     };
 
-    floatx4 acc[kMaxSub];            // per active index u (sub-tile act[u])
+    floatx4 acc[kSub];            // per active index u (sub-tile act[u])
 #pragma unroll
-    for (int u = 0; u < kMaxSub; ++u) acc[u] = floatx4{0, 0, 0, 0};
+    for (int u = 0; u < kSub; ++u) acc[u] = floatx4{0, 0, 0, 0};
 
     // This lane's weight row within the tile, and where its words sit in a slot.
     // Step j, lane group q reads elements 32j + 8q .. +7 of the row's slab:
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
           }
         }
 #pragma unroll
-        for (int u = 0; u < kMaxSub; ++u) {
+        for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
           // One chain per active sub-tile: the bias product and the
           // zero-point product accumulate into the same partial.
@@ -439,17 +447,17 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
       float* xch = reinterpret_cast<float*>(ring);
       if (rs == 1) {
 #pragma unroll
-        for (int u = 0; u < kMaxSub; ++u)
-          *reinterpret_cast<floatx4*>(xch + (((wave & 3) * kMaxSub + u) * kWave + lane) * 4) = acc[u];
+        for (int u = 0; u < kSub; ++u)
+          *reinterpret_cast<floatx4*>(xch + (((wave & 3) * kSub + u) * kWave + lane) * 4) = acc[u];
       }
       lds_barrier();
       if (rs == 0) {
 #pragma unroll
-        for (int u = 0; u < kMaxSub; ++u) {
+        for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
           const int r = cols[16 * act[u] + n];
           if (r < 0) continue;
-          const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kMaxSub + u) * kWave + lane) * 4);
+          const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kSub + u) * kWave + lane) * 4);
           uint32_t hi2[2], lo2[2];
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {
@@ -468,7 +476,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm(const GemmParams p)
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kMaxSub; ++u) {
+      for (int u = 0; u < kSub; ++u) {
         if (u >= nact) break;
         const int r = cols[16 * act[u] + n];
         if (r < 0) continue;
@@ -534,31 +542,44 @@ bool group_ok(int K, int g, int slab) {
   return g < slab ? (slab % g) == 0 : (g % slab) == 0;
 }
 
-template <int kFmt, bool kGateUp, int kPlanes, int kSteps>
-hipError_t launch_gemm_fmt(const GemmParams& gp, int wgs, hipStream_t stream) {
+template <int kFmt, bool kGateUp, int kPlanes, int kSteps, int kRing>
+hipError_t launch_gemm_ring(const GemmParams& gp, int wgs, hipStream_t stream) {
+  if constexpr (kFmt == MOE_W_MXFP8) {
+    hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 1, kRing>), dim3(wgs), dim3(kGemmThreads), 0,
+                       stream, gp);
+    return hipGetLastError();
+  }
   switch (flush_steps(gp.g, kSteps)) {
     case 1:
-      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 1>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 1, kRing>), dim3(wgs), dim3(kGemmThreads), 0,
+                         stream, gp);
       break;
     case 2:
-      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 2>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 2, kRing>), dim3(wgs), dim3(kGemmThreads), 0,
+                         stream, gp);
       break;
     default:
-      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, kSteps>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, kSteps, kRing>), dim3(wgs),
+                         dim3(kGemmThreads), 0, stream, gp);
       break;
   }
   return hipGetLastError();
 }
 
+// MXFP8 blocks are 32 elements: one scaled partial per MFMA step. Layers
+// aligned with b <= 16 have one 16-column sub-tile per block, whose ring
+// slots are small: a 36 KB ring (int4; 40 KB for MXFP8's wider weight rows)
+// keeps two or more slots in flight and lets three workgroups share a CU
+// (more tasks per round).
 template <bool kGateUp, int kPlanes, int kSteps>
 hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t stream) {
-  // MXFP8 blocks are 32 elements: one scaled partial per MFMA step.
   if (fmt == MOE_W_MXFP8) {
-    hipLaunchKernelGGL((grouped_gemm<MOE_W_MXFP8, kGateUp, kPlanes, kSteps, 1>), dim3(wgs), dim3(kGemmThreads), 0,
-                       stream, gp);
-    return hipGetLastError();
+    if (gp.b <= 16)
+      return launch_gemm_ring<MOE_W_MXFP8, kGateUp, kPlanes, kSteps, kSmallRingMxBytes>(gp, wgs, stream);
+    return launch_gemm_ring<MOE_W_MXFP8, kGateUp, kPlanes, kSteps, kRingBytes>(gp, wgs, stream);
   }
-  return launch_gemm_fmt<MOE_W_INT4_AWQ, kGateUp, kPlanes, kSteps>(gp, wgs, stream);
+  if (gp.b <= 16) return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, kPlanes, kSteps, kSmallRingBytes>(gp, wgs, stream);
+  return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, kPlanes, kSteps, kRingBytes>(gp, wgs, stream);
 }
 
 constexpr int kGateUpSteps = 4;   // 128-element slabs
