@@ -25,8 +25,9 @@
  *   - Host-checkable errors return a status synchronously and enqueue nothing.
  *     Launch failures return MOE_ERR_HIP. M == 0 is a no-op returning MOE_OK.
  *   - Data-dependent conditions are defined behaviour, not errors: an expert
- *     ID outside [0, E) marks an invalid route, which alignment skips and
- *     which contributes nothing to the output.
+ *     ID outside the experts held here ([expert_base, expert_base + E); [0, E)
+ *     for moe_align) marks an invalid route, which alignment skips and which
+ *     contributes nothing to the output.
  *   - Results are deterministic: the same inputs, shapes and path give the
  *     same output bytes on every run and for every workgroup cap (no
  *     floating-point atomics; every reduction has a fixed order).

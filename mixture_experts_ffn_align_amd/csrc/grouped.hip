@@ -5,40 +5,45 @@
 // Section 3.4: grouped GEMM over routing-dependent token counts, weights as
 // the left operand so Y_e^T = W_e X_e^T).
 //
-// One kernel template serves both GEMMs. A workgroup takes one aligned block
-// (b <= 64 routes of one expert: four 16-column sub-tiles) and 64 output rows;
-// wave w owns rows 16w..16w+15 (for gate/up: those 16 neurons' gate rows and
-// their up rows). Every product is v_mfma_f32_16x16x32_bf16 with the expert's
-// weight rows on A and the block's columns on B:
+// One kernel template serves both GEMMs. A workgroup of eight waves takes one
+// aligned block (b <= 64 routes of one expert: up to four 16-column
+// sub-tiles) and a tile of two row sets of 64 weight rows (gate/up: the gate
+// rows and the up rows of 64 neurons; down: the two halves of 128 output
+// rows); wave w owns rows 16 (w % 4) .. +15 of row set w / 4. Every product
+// is v_mfma_f32_16x16x32_bf16 with the expert's weight rows on A and the
+// block's columns on B:
 //   A lane l: weight row l%16, 8 reduction elements of lane group l/16;
 //   B lane l: column l%16, the same 8 reduction elements;
 //   D lane l: rows 4*(l/16)+i (i < 4) of column l%16.
-// The reduction runs in slabs of 128 elements, four MFMA steps of 32 each
-// (step j, lane group q: elements 32j+8q .. 32j+8q+7 of the slab), so every
-// step lies inside one quantisation group whenever g is a multiple of 32.
+// The reduction runs in slabs of 128 (gate/up) or 64 (down) elements, MFMA
+// steps of 32 (step j, lane group q: elements 32j+8q .. 32j+8q+7 of the
+// slab), so every step lies inside one quantisation group whenever g is a
+// multiple of 32.
 //
-// Data movement: the weight rows of a wave (16 rows x 64 bytes per slab and
-// row set) and the block's activation rows (16 bytes per lane, per sub-tile,
-// step and plane) go global -> LDS with 16-byte LDS-DMA loads into rings of
-// kD slabs, issued kD-1 slabs ahead; nothing passes through VGPRs. Each
-// slab costs one wait on the wave's own loads (an exact vmcnt: the loads of
-// the later slabs stay in flight) and one workgroup barrier. The activation
-// loads of a slab are spread evenly over the four waves and cover only
-// sub-tiles that hold a valid route; the tile's scales and zeros arrive with
-// the first slab. Sub-tiles with no valid route are skipped.
+// Data movement: the tile's weight rows and the block's activation rows
+// (16 bytes per lane, per active sub-tile, step and plane) go global -> LDS
+// with 16-byte LDS-DMA loads into one ring of slab-sized slots, issued
+// depth - 1 slabs ahead; nothing passes through VGPRs. The depth follows
+// from the slot size (the slot holds only active sub-tiles). Each slab costs
+// one wait on the wave's own loads (an exact vmcnt: the loads of the later
+// slabs stay in flight) and one LDS-only workgroup barrier. Weight and
+// activation loads are spread over the eight waves; the tile's scales and
+// zeros arrive with the first slab. Blocks of one sub-tile (b <= 16) use a
+// smaller ring and fewer registers so that three workgroups share a CU.
 //
 // The int4 words become bf16 (128 + q) pairs with one AND-OR each (AWQ
 // nibble order) and a second MFMA per step adds -(128 + z) times the same
 // activations, so a group's partial holds sum x (q - z); it is scaled by the
-// group scale in fp32.
+// group scale in fp32. MXFP8 codes convert exactly to bf16; the partial is
+// scaled by the block's power of two.
 // gate/up: B is x; the epilogue writes silu(gate) * up for every valid route
 //   as a bf16 hi/lo pair (a = hi + lo to within 2^-17 relative).
 // down: B is the hi and the lo plane of the intermediate (both accumulate
 //   into the same partial); each route's yhat row is written once.
 // combine: y[t] = sum over j ascending of w[t,j] * yhat[t*k+j].
-// Workgroups whose block lies past num_padded (read on the device) exit at
-// once, so the grid can be sized from the host-known capacity. No
-// floating-point atomics; every sum has a fixed order.
+// Workgroups whose block lies past num_padded (read on the device) skip it,
+// so the grid can be sized from the host-known capacity. No floating-point
+// atomics; every sum has a fixed order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,9 +51,8 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kTileRows = 16 * kWaves;   // output rows per workgroup
+constexpr int kThreads = 256;            // combine workgroup
+constexpr int kTileRows = 64;            // weight rows per row set of a GEMM tile (four waves of 16)
 constexpr int kMaxTok = 64;              // block size limit: four 16-column sub-tiles
 constexpr int kMaxSub = kMaxTok / 16;
 constexpr int kMaxGpr = 32;              // K / g limit (the tile's scales live in LDS)
