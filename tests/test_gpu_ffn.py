@@ -72,6 +72,11 @@ RAGGED = [
     dict(M=200, H=256, I=128, E=4, k=2, b=64, g=64),
     dict(M=150, H=512, I=256, E=4, k=2, b=64, g=32),
     dict(M=120, H=256, I=128, E=4, k=2, b=32, g=64),
+    # The most experts the library takes (2048) with 16 routes per token (the
+    # decode path's limit), and one expert holding every route in many full
+    # blocks of 64.
+    dict(M=40, H=256, I=128, E=2048, k=16, b=8, g=64),
+    dict(M=300, H=256, I=128, E=1, k=1, b=64, g=64),
     # MXFP8 weights (E4M3 + E8M0 per 32): several lane layouts, k > 8, full blocks.
     dict(M=5, H=256, I=128, E=8, k=2, b=8, g=32, fmt="mxfp8"),
     dict(M=3, H=512, I=448, E=16, k=5, b=8, g=32, fmt="mxfp8"),
