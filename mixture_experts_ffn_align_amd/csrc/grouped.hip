@@ -175,6 +175,9 @@ void grouped_gemm(const GemmParams p) {
   constexpr int kZpStride = kTileRows * kMaxGpr;       // bytes per row set (u8 zeros)
   constexpr int kADma = kABytes / 1024;                // weight DMAs per slab
   static_assert(kADma == 4 || kADma == 8 || kADma == 16, "weight DMAs per slab");
+  // The pipeline keeps at least two slots in flight at the largest slot (every
+  // sub-tile active); the depth computed per task relies on it.
+  static_assert(kRing >= 2 * (kABytes + kSub * kPlanes * kSteps * 1024), "ring holds two slabs");
   __shared__ __align__(16) unsigned char ring[kRing];
   __shared__ __align__(16) unsigned char ssh[2 * kScStride];
   __shared__ __align__(16) unsigned char szz[2 * kZpStride];
@@ -248,7 +251,7 @@ void grouped_gemm(const GemmParams p) {
     const int nbdma = nact * kPlanes * kSteps;                 // activation DMAs per slab
     const int slot_bytes = kABytes + nbdma * 1024;
     const int depth_fit = kRing / slot_bytes;
-    const int depth = depth_fit < kMaxDepth ? depth_fit : kMaxDepth;   // >= 2 by construction
+    const int depth = depth_fit < kMaxDepth ? depth_fit : kMaxDepth;   // >= 2 (static_assert above)
     // This wave's DMAs per slab: weight DMA i goes to wave i, activation DMA
     // i to wave i % 8.
     const int my_b = nbdma > wave ? (nbdma - wave + kGemmWaves - 1) / kGemmWaves : 0;
