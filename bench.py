@@ -317,13 +317,13 @@ def grouped_sweep(fmt):
             xv = rng.standard_normal((G, N, H)).astype(np.float32)
             xb = torch.from_numpy((xv.view(np.uint32) >> 16).astype(np.uint16).view(np.int16)).cuda() \
                 .view(torch.bfloat16)
-            hi = torch.zeros((G, N, I), dtype=torch.bfloat16, device="cuda")
-            lo = torch.zeros_like(hi)
+            a16 = torch.zeros((G, N, I), dtype=torch.float16, device="cuda")
+            asc = torch.zeros((G, N, I // 128, 4), dtype=torch.float32, device="cuda")
             yb = torch.zeros((G, N, H), dtype=torch.float32, device="cuda")
             descs = [L.desc(1) for L in layers]
             stages = {
-                "gate_up": (lambda d: moe.moe_ffn_gate_up_batched(d, xb, counts, hi, lo), 2 * I, H, per13),
-                "down": (lambda d: moe.moe_ffn_down_batched(d, hi, lo, counts, yb), H, I, per2),
+                "gate_up": (lambda d: moe.moe_ffn_gate_up_batched(d, xb, counts, a16, asc), 2 * I, H, per13),
+                "down": (lambda d: moe.moe_ffn_down_batched(d, a16, asc, counts, yb), H, I, per2),
             }
             for name, (fn, Mdim, Kdim, per) in stages.items():
                 stream = torch.cuda.Stream()

@@ -70,9 +70,11 @@ typedef enum {
 
 typedef enum {
   MOE_PATH_AUTO = 0,     /* decode for M <= moe_ffn_auto_decode_max_m(), else grouped; when the
-                            decode path's shape rules fail, grouped */
+                            chosen path's shape rules fail, the other path */
   MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
-  MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised bf16 MFMA grouped GEMMs + combine */
+  MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised MFMA grouped GEMMs + combine; needs H and I
+                            multiples of 128, b <= 64 and (int4) K/group <= 32 with group
+                            dividing 128 or a multiple of it */
 } moe_path;
 
 /* One projection's resident packed weights for all E experts. */
@@ -218,21 +220,22 @@ MOE_API moe_status moe_ffn_down_combine(const moe_ffn_desc* d, const int32_t* to
  * batched operand; counts[e] is read on the device and clamped to
  * [0, capacity]; rows past it are neither read nor written.
  *   xb        bf16 [E][capacity][H]            (gate/up input)
- *   a_hi/a_lo bf16 [E][capacity][I] planes of silu(gate)*up = hi + lo
- *             (gate/up output, down input; the layout of moe_ffn_intermediate)
+ *   a16       fp16 [E][capacity][I] and
+ *   a_scale   fp32 [E][capacity][I/128][4]: silu(gate)*up in format 2 of
+ *             moe_ffn_intermediate (gate/up output, down input)
  *   yb        fp32 [E][capacity][H]            (down output, before any combine)
  *   counts    int32 [E] device
  * Uses d->H, I, E, b (rows per tile, <= 64), w13 / w2 and max_workgroups; M, k,
  * path and expert_base are not used. Same arithmetic, per row, as the grouped
  * path of moe_ffn_forward.
  * Errors: MOE_ERR_INVALID_ARG (null or misaligned pointers: 16 bytes for the
- * row arrays; capacity < 1; the layer checks of moe_ffn_forward),
+ * row arrays and a_scale; capacity < 1; the layer checks of moe_ffn_forward),
  * MOE_ERR_UNSUPPORTED (grouped-path shape rules; E*capacity > INT32_MAX),
  * MOE_ERR_HIP. */
 MOE_API moe_status moe_ffn_gate_up_batched(const moe_ffn_desc* d, const uint16_t* xb, const int32_t* counts,
-                                           int32_t capacity, uint16_t* a_hi, uint16_t* a_lo,
+                                           int32_t capacity, uint16_t* a16, float* a_scale,
                                            hipStream_t stream);
-MOE_API moe_status moe_ffn_down_batched(const moe_ffn_desc* d, const uint16_t* a_hi, const uint16_t* a_lo,
+MOE_API moe_status moe_ffn_down_batched(const moe_ffn_desc* d, const uint16_t* a16, const float* a_scale,
                                         const int32_t* counts, int32_t capacity, float* yb,
                                         hipStream_t stream);
 
@@ -242,12 +245,19 @@ MOE_API int32_t moe_ffn_kernel_count(const moe_ffn_desc* d);
 /* Name of kernel i of moe_ffn_forward for this description, or NULL. */
 MOE_API const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
 
-/* Where a forward call leaves the route-indexed intermediate silu(gate)*up
- * inside the workspace (rows of invalid routes are unspecified): a bf16 hi
- * plane [M*k][I] at *offset and a bf16 lo plane at *lo_offset, the value being
- * hi + lo (within 2^-17 relative). *format is 1 (the only layout; 0 is
- * reserved for an fp32 plane). */
-MOE_API moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* lo_offset,
+/* Where a forward call leaves the route-indexed intermediate a = silu(gate)*up
+ * inside the workspace (rows of invalid routes are unspecified), and in which
+ * format (0 is reserved for an fp32 plane):
+ *   1 (decode path): a bf16 hi plane [M*k][I] at *offset and a bf16 lo plane
+ *     at *aux_offset; a = hi + lo within 2^-17 relative.
+ *   2 (grouped path): an fp16 plane [M*k][I] at *offset and fp32 multipliers
+ *     [M*k][I/128][4] at *aux_offset; element i of route r is
+ *     fp16[r][i] * mult[r][i/128][(i/64) % 2] (entries 2 and 3 unused). Each
+ *     64-element chunk is scaled by a power of two that puts its largest
+ *     magnitude in [2^14, 2^15) before rounding to fp16, so every element is
+ *     within 2^-11 relative of the fp32 value (elements below 2^-28 of their
+ *     chunk's largest aside). */
+MOE_API moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* aux_offset,
                                 int32_t* format);
 
 /* Largest M for which MOE_PATH_AUTO picks the decode path. */

@@ -233,17 +233,19 @@ def moe_ffn_down_combine(desc: moe_ffn_desc, topk_ids, topk_w, y, ws, stream=Non
            "moe_ffn_down_combine")
 
 
-def moe_ffn_gate_up_batched(desc: moe_ffn_desc, xb, counts, a_hi, a_lo, stream=None) -> None:
-    """xb [E, capacity, H] bf16, counts [E] int32 (device), a_hi / a_lo [E, capacity, I]."""
+def moe_ffn_gate_up_batched(desc: moe_ffn_desc, xb, counts, a16, a_scale, stream=None) -> None:
+    """xb [E, capacity, H] bf16, counts [E] int32 (device), a16 [E, capacity, I]
+    fp16 and a_scale [E, capacity, I/128, 4] fp32 (intermediate format 2)."""
     _check(lib().moe_ffn_gate_up_batched(ctypes.byref(desc), _ptr(xb), _ptr(counts), xb.shape[1],
-                                         _ptr(a_hi), _ptr(a_lo), _stream(stream)),
+                                         _ptr(a16), _ptr(a_scale), _stream(stream)),
            "moe_ffn_gate_up_batched")
 
 
-def moe_ffn_down_batched(desc: moe_ffn_desc, a_hi, a_lo, counts, yb, stream=None) -> None:
-    """a_hi / a_lo [E, capacity, I] bf16 planes, counts [E] int32, yb [E, capacity, H] fp32."""
-    _check(lib().moe_ffn_down_batched(ctypes.byref(desc), _ptr(a_hi), _ptr(a_lo), _ptr(counts),
-                                      a_hi.shape[1], _ptr(yb), _stream(stream)),
+def moe_ffn_down_batched(desc: moe_ffn_desc, a16, a_scale, counts, yb, stream=None) -> None:
+    """a16 [E, capacity, I] fp16 and a_scale [E, capacity, I/128, 4] fp32, counts [E]
+    int32, yb [E, capacity, H] fp32."""
+    _check(lib().moe_ffn_down_batched(ctypes.byref(desc), _ptr(a16), _ptr(a_scale), _ptr(counts),
+                                      a16.shape[1], _ptr(yb), _stream(stream)),
            "moe_ffn_down_batched")
 
 
@@ -257,10 +259,11 @@ def moe_ffn_kernel_name(desc: moe_ffn_desc, i: int) -> str | None:
 
 
 def moe_ffn_intermediate(desc: moe_ffn_desc) -> tuple[int, int, int]:
-    off, lo, fmt = _c_size(0), _c_size(0), _c_i32(0)
-    _check(lib().moe_ffn_intermediate(ctypes.byref(desc), ctypes.byref(off), ctypes.byref(lo),
+    """(offset, aux_offset, format) of the intermediate in the workspace."""
+    off, aux, fmt = _c_size(0), _c_size(0), _c_i32(0)
+    _check(lib().moe_ffn_intermediate(ctypes.byref(desc), ctypes.byref(off), ctypes.byref(aux),
                                       ctypes.byref(fmt)), "moe_ffn_intermediate")
-    return int(off.value), int(lo.value), int(fmt.value)
+    return int(off.value), int(aux.value), int(fmt.value)
 
 
 def moe_ffn_auto_decode_max_m() -> int:

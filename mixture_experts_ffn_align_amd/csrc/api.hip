@@ -30,7 +30,7 @@ struct Layout {
   int path = MOE_PATH_DECODE;
   size_t cap = 0;        // alignment capacity (grouped)
   size_t off_sorted = 0, off_blocks = 0, off_npad = 0, off_align_ws = 0, align_ws = 0;
-  size_t off_a = 0, off_a_lo = 0, off_yhat = 0;
+  size_t off_a = 0, off_aux = 0, off_yhat = 0;   // intermediate (see moe_ffn_intermediate), yhat
   size_t total = 0;
 };
 
@@ -83,8 +83,9 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
 
   int path = d->path;
   if (path == MOE_PATH_AUTO) {
+    // The size-based choice, else the other path when its shape rules fail.
     path = auto_path(d);
-    if (!shape_ok(path, d)) path = MOE_PATH_GROUPED;
+    if (!shape_ok(path, d)) path = path == MOE_PATH_DECODE ? MOE_PATH_GROUPED : MOE_PATH_DECODE;
   }
   if (need_align_buffers) path = MOE_PATH_GROUPED;
   L->path = path;
@@ -92,8 +93,8 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   if (!tasks_fit(path, d, mk)) return MOE_ERR_UNSUPPORTED;
   if (path == MOE_PATH_DECODE) {
     L->off_a = 0;
-    L->off_a_lo = round256(size_t(mk) * d->I * sizeof(uint16_t));
-    L->total = L->off_a_lo + round256(size_t(mk) * d->I * sizeof(uint16_t));
+    L->off_aux = round256(size_t(mk) * d->I * sizeof(uint16_t));
+    L->total = L->off_aux + round256(size_t(mk) * d->I * sizeof(uint16_t));
     if (L->total == 0) L->total = 256;
     return MOE_OK;
   }
@@ -105,7 +106,7 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   L->align_ws = moe::align_ws_bytes(static_cast<int>(mk), d->E);
   L->off_align_ws = o; o += L->align_ws;
   L->off_a = o;      o += round256(size_t(mk) * d->I * sizeof(uint16_t));
-  L->off_a_lo = o;   o += round256(size_t(mk) * d->I * sizeof(uint16_t));
+  L->off_aux = o;    o += round256(size_t(mk) * (d->I / 128) * 4 * sizeof(float));
   L->off_yhat = o;   o += round256(size_t(mk) * d->H * sizeof(float));
   L->total = o;
   return MOE_OK;
@@ -142,7 +143,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
   if (L.path == MOE_PATH_DECODE) {
     moe::DecodeArgs p{};
     p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
-    p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_a_lo); p.y = y;
+    p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_aux); p.y = y;
     p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k;
     p.ebase = d->expert_base;
     p.max_workgroups = d->max_workgroups;
@@ -159,7 +160,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
   moe::GroupedArgs p{};
   const int64_t mk = int64_t(d->M) * d->k;
   p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
-  p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_a_lo);
+  p.a16 = at<uint16_t>(ws, L.off_a); p.a_scale = at<float>(ws, L.off_aux);
   p.yhat = at<float>(ws, L.off_yhat); p.y = y;
   p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k; p.b = d->b;
   p.ebase = d->expert_base;
@@ -377,29 +378,29 @@ moe::GroupedArgs batched_args(const moe_ffn_desc* d) {
 extern "C" {
 
 moe_status moe_ffn_gate_up_batched(const moe_ffn_desc* d, const uint16_t* xb, const int32_t* counts,
-                                   int32_t capacity, uint16_t* a_hi, uint16_t* a_lo, hipStream_t stream) {
+                                   int32_t capacity, uint16_t* a16, float* a_scale, hipStream_t stream) {
   moe_status st = validate_batched(d, capacity);
   if (st != MOE_OK) return st;
-  if (xb == nullptr || counts == nullptr || a_hi == nullptr || a_lo == nullptr) return MOE_ERR_INVALID_ARG;
-  if (!aligned(xb, 16) || !aligned(a_hi, 16) || !aligned(a_lo, 16) || !aligned(counts, 4))
+  if (xb == nullptr || counts == nullptr || a16 == nullptr || a_scale == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(xb, 16) || !aligned(a16, 16) || !aligned(a_scale, 16) || !aligned(counts, 4))
     return MOE_ERR_INVALID_ARG;
   moe::GroupedArgs p = batched_args(d);
   p.x = xb;
-  p.a_hi = a_hi;
-  p.a_lo = a_lo;
+  p.a16 = a16;
+  p.a_scale = a_scale;
   return hip_status(moe::launch_grouped_gate_up_batched(p, counts, capacity, stream));
 }
 
-moe_status moe_ffn_down_batched(const moe_ffn_desc* d, const uint16_t* a_hi, const uint16_t* a_lo,
+moe_status moe_ffn_down_batched(const moe_ffn_desc* d, const uint16_t* a16, const float* a_scale,
                                 const int32_t* counts, int32_t capacity, float* yb, hipStream_t stream) {
   moe_status st = validate_batched(d, capacity);
   if (st != MOE_OK) return st;
-  if (a_hi == nullptr || a_lo == nullptr || counts == nullptr || yb == nullptr) return MOE_ERR_INVALID_ARG;
-  if (!aligned(a_hi, 16) || !aligned(a_lo, 16) || !aligned(yb, 16) || !aligned(counts, 4))
+  if (a16 == nullptr || a_scale == nullptr || counts == nullptr || yb == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(a16, 16) || !aligned(a_scale, 16) || !aligned(yb, 16) || !aligned(counts, 4))
     return MOE_ERR_INVALID_ARG;
   moe::GroupedArgs p = batched_args(d);
-  p.a_hi = const_cast<uint16_t*>(a_hi);   // read only: the down GEMM's input planes
-  p.a_lo = const_cast<uint16_t*>(a_lo);
+  p.a16 = const_cast<uint16_t*>(a16);        // read only: the down GEMM's input
+  p.a_scale = const_cast<float*>(a_scale);
   p.yhat = yb;
   return hip_status(moe::launch_grouped_down_batched(p, counts, capacity, stream));
 }
@@ -422,15 +423,15 @@ const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i) {
   return (i >= 0 && i < 4) ? kGrouped[i] : nullptr;
 }
 
-moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* lo_offset,
+moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* aux_offset,
                                 int32_t* format) {
-  if (offset == nullptr || lo_offset == nullptr || format == nullptr) return MOE_ERR_INVALID_ARG;
+  if (offset == nullptr || aux_offset == nullptr || format == nullptr) return MOE_ERR_INVALID_ARG;
   Layout L;
   const moe_status st = validate(d, &L, false);
   if (st != MOE_OK) return st;
   *offset = L.off_a;
-  *lo_offset = L.off_a_lo;
-  *format = 1;
+  *aux_offset = L.off_aux;
+  *format = L.path == MOE_PATH_DECODE ? 1 : 2;
   return MOE_OK;
 }
 

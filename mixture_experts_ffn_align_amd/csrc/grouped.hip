@@ -10,36 +10,40 @@
 // sub-tiles) and a tile of two row sets of 64 weight rows (gate/up: the gate
 // rows and the up rows of 64 neurons; down: the two halves of 128 output
 // rows); wave w owns rows 16 (w % 4) .. +15 of row set w / 4. Every product
-// is v_mfma_f32_16x16x32_bf16 with the expert's weight rows on A and the
-// block's columns on B:
+// is a 16x16x32 MFMA (bf16 for gate/up, fp16 for down) with the expert's
+// weight rows on A and the block's columns on B:
 //   A lane l: weight row l%16, 8 reduction elements of lane group l/16;
 //   B lane l: column l%16, the same 8 reduction elements;
 //   D lane l: rows 4*(l/16)+i (i < 4) of column l%16.
-// The reduction runs in slabs of 128 (gate/up) or 64 (down) elements, MFMA
-// steps of 32 (step j, lane group q: elements 32j+8q .. 32j+8q+7 of the
-// slab), so every step lies inside one quantisation group whenever g is a
-// multiple of 32.
+// The reduction runs in slabs of 128 elements, MFMA steps of 32 (step j,
+// lane group q: elements 32j+8q .. 32j+8q+7 of the slab), so every step lies
+// inside one quantisation group whenever g is a multiple of 32.
 //
 // Data movement: the tile's weight rows and the block's activation rows
-// (16 bytes per lane, per active sub-tile, step and plane) go global -> LDS
-// with 16-byte LDS-DMA loads into one ring of slab-sized slots, issued
-// depth - 1 slabs ahead; nothing passes through VGPRs. The depth follows
-// from the slot size (the slot holds only active sub-tiles). Each slab costs
-// one wait on the wave's own loads (an exact vmcnt: the loads of the later
-// slabs stay in flight) and one LDS-only workgroup barrier. Weight and
-// activation loads are spread over the eight waves; the tile's scales and
-// zeros arrive with the first slab. Blocks of one sub-tile (b <= 16) use a
-// smaller ring and fewer registers so that three workgroups share a CU.
+// (16 bytes per lane, per active sub-tile and step) go global -> LDS with
+// 16-byte LDS-DMA loads into one ring of slab-sized slots, issued depth - 1
+// slabs ahead; nothing passes through VGPRs. The depth follows from the slot
+// size (the slot holds only active sub-tiles). Each slab costs one wait on
+// the wave's own loads (an exact vmcnt: the loads of the later slabs stay in
+// flight) and one LDS-only workgroup barrier. Weight and activation loads
+// are spread over the eight waves; the tile's scales and zeros arrive with
+// the first slab. Blocks of one sub-tile (b <= 16) use a smaller ring and
+// fewer registers so that three workgroups share a CU.
 //
-// The int4 words become bf16 (128 + q) pairs with one AND-OR each (AWQ
-// nibble order) and a second MFMA per step adds -(128 + z) times the same
-// activations, so a group's partial holds sum x (q - z); it is scaled by the
-// group scale in fp32. MXFP8 codes convert exactly to bf16; the partial is
-// scaled by the block's power of two.
-// gate/up: B is x; the epilogue writes silu(gate) * up for every valid route
-//   as a bf16 hi/lo pair (a = hi + lo to within 2^-17 relative).
-// down: B is the hi and the lo plane of the intermediate (both accumulate
-//   into the same partial); each route's yhat row is written once.
+// The int4 words become (128 + q) pairs with one AND-OR each (AWQ nibble
+// order; bf16 or fp16, both exact) and a second MFMA per step adds
+// -(128 + z) times the same activations, so a group's partial holds
+// sum x (q - z); it is scaled by the group scale in fp32. MXFP8 codes convert
+// exactly to bf16 or fp16; the partial is scaled by the block's power of two.
+// gate/up: B is x (bf16); the epilogue writes a = silu(gate) * up for every
+//   valid route as one fp16 plane: each route's 64 neurons of the tile are
+//   multiplied by a power of two that puts their largest magnitude in
+//   [2^14, 2^15) (no overflow; relative rounding 2^-11 for every value of
+//   the chunk down to 2^-28 of its largest), and the inverse power of two is
+//   stored beside it.
+// down: B is that fp16 plane, plus per slab one page with each column's two
+//   chunk multipliers, applied to the partial of each 64-element chunk;
+//   each route's yhat row is written once.
 // combine: y[t] = sum over j ascending of w[t,j] * yhat[t*k+j].
 // Workgroups whose block lies past num_padded (read on the device) skip it,
 // so the grid can be sized from the host-known capacity. No floating-point
@@ -57,23 +61,80 @@ constexpr int kMaxTok = 64;              // block size limit: four 16-column sub
 constexpr int kMaxSub = kMaxTok / 16;
 constexpr int kMaxGpr = 32;              // K / g limit (the tile's scales live in LDS)
 
-__device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+constexpr int kSteps = 4;                // 32-element MFMA steps per slab
+constexpr int kSlabK = 32 * kSteps;      // reduction elements per slab
+
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+
+// A and B travel as raw 16-byte words; kHalf selects the fp16 MFMA (down:
+// the intermediate is fp16) or the bf16 one (gate/up: x is bf16).
+template <bool kHalf>
+__device__ __forceinline__ floatx4 mfma16(const uint4& a, const uint4& b, const floatx4& c) {
+  if constexpr (kHalf)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
 }
 
-// One packed word -> eight bf16 (128 + q), element order.
-__device__ __forceinline__ bf16x8 bias_pairs(uint32_t w, uint32_t m) {
-  uint32_t p[4];
-  unpack8_bias128_m(w, m, p);
-  return __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+// Nibble mask of bias_pairs, to be held in a VGPR (one v_and_or_b32 per pair).
+template <bool kHalf>
+constexpr uint32_t kNibMask = kHalf ? 0x00780078u : 0x000F000Fu;
+
+// One packed word -> eight (128 + q) values in element order. AWQ's nibble
+// order puts elements 2i and 2i+1 in slots i and i+4 (bits 4i and 4i+16).
+// bf16: 0x4300 is 128.0 with a mantissa step of 1, so (w >> 4i) & 0x000F000F
+// OR 0x43004300 is the pair. fp16: 0x5800 is 128.0 with a step of 1/8, so
+// the nibbles go three bits higher (mask 0x00780078).
+template <bool kHalf>
+__device__ __forceinline__ uint4 bias_pairs(uint32_t w, uint32_t m) {
+  if constexpr (kHalf) {
+    const uint32_t c = 0x58005800u;
+    return make_uint4(((w << 3) & m) | c, ((w >> 1) & m) | c, ((w >> 5) & m) | c, ((w >> 9) & m) | c);
+  } else {
+    uint32_t p[4];
+    unpack8_bias128_m(w, m, p);
+    return make_uint4(p[0], p[1], p[2], p[3]);
+  }
 }
 
-// Eight copies of the bf16 value -(128 + z), z in 0..15.
-__device__ __forceinline__ bf16x8 neg_zero_pairs(uint32_t z) {
-  const uint32_t h = 0xC300u | z;
+// Eight copies of -(128 + z), z in 0..15 (bf16 0xC300 | z, fp16 0xD800 | 8z).
+template <bool kHalf>
+__device__ __forceinline__ uint4 neg_zero_pairs(uint32_t z) {
+  const uint32_t h = kHalf ? (0xD800u | (z << 3)) : (0xC300u | z);
   const uint32_t pr = h | (h << 16);
-  return __builtin_bit_cast(bf16x8, make_uint4(pr, pr, pr, pr));
+  return make_uint4(pr, pr, pr, pr);
 }
+
+// Two E4M3 codes (the low or the high 16 bits of w) -> an fp16 pair, exact.
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi));
+}
+
+// Four E4M3 codes of each of two words -> eight bf16 or fp16 values.
+template <bool kHalf>
+__device__ __forceinline__ uint4 fp8_operand(uint32_t w0, uint32_t w1) {
+  if constexpr (kHalf)
+    return make_uint4(fp8x2_to_f16x2<false>(w0), fp8x2_to_f16x2<true>(w0), fp8x2_to_f16x2<false>(w1),
+                      fp8x2_to_f16x2<true>(w1));
+  else
+    return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                      fp8x2_to_bf16x2<true>(w1));
+}
+
+// Power-of-two shift t of a chunk whose largest magnitude is m: m * 2^t lies
+// in [2^14, 2^15) (t = 14 - (exponent of m)); zero, infinite and NaN chunks
+// keep t = 0, and t stays in [-126, 126] so that 2^t and 2^-t are normal.
+__device__ __forceinline__ int chunk_shift(float m) {
+  const int eb = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu);
+  const int t = (m > 0.0f && eb < 255) ? 141 - eb : 0;
+  return t < -126 ? -126 : (t > 126 ? 126 : t);
+}
+
+__device__ __forceinline__ float pow2f(int t) { return __uint_as_float(static_cast<uint32_t>(t + 127) << 23); }
 
 // LDS byte address of a __shared__ object (low half of its generic address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -121,8 +182,8 @@ __device__ __forceinline__ void wait_vm_le(int n) {
 }
 
 struct GemmParams {
-  const uint16_t* b0;            // B rows (bf16, K per row): x [M] or a_hi [Mk]
-  const uint16_t* b1;            // second plane (a_lo) or null
+  const uint16_t* b0;            // B rows (K per row): x [M] bf16, or the intermediate [Mk] fp16
+  const float* bsc;              // down: chunk multipliers of the B rows [Mk][K/128][4], else null
   const int32_t* sorted;         // aligned rows (null in the batched layout)
   const int32_t* blocks;
   const int32_t* num_padded;
@@ -132,8 +193,8 @@ struct GemmParams {
   const unsigned char* q;        // int4: u32 [E][rows][K/8]; MXFP8: E4M3 [E][rows][K]
   const unsigned char* sc;       // int4: fp16 [E][rows][K/g]; MXFP8: E8M0 [E][rows][K/32]
   const uint8_t* zp;
-  uint16_t* a_hi;                // gate/up output planes [Mk][I]
-  uint16_t* a_lo;
+  uint16_t* a16;                 // gate/up output: fp16 [Mk][I], scaled per 64-neuron chunk
+  float* a_scale;                // gate/up output: [Mk][I/128][4], entries 0, 1 undo the two chunks' scaling
   float* yhat;                   // down output [Mk][H]
   int mk, k, E, b, nblk;
   int ntile;                     // tiles per block
@@ -146,28 +207,41 @@ struct GemmParams {
 
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * kWave;
-constexpr int kRingBytes = 64 * 1024;        // two workgroups per CU
-constexpr int kSmallRingBytes = 36 * 1024;   // int4 with b <= 16 (one sub-tile): three per CU
-constexpr int kSmallRingMxBytes = 40 * 1024; // MXFP8 with b <= 16: three per CU
 constexpr int kMaxDepth = 8;
+
+// LDS ring of one GEMM instantiation. A slot holds one slab: the tile's 128
+// weight rows, 1 KB per (active sub-tile, step) of activations and, for the
+// down GEMM, a 1 KB page of chunk multipliers. Blocks of up to four
+// sub-tiles (b <= 64) get at least 64 KB and two slots at the largest slot
+// (two workgroups per CU); blocks of one sub-tile (b <= 16) get three int4
+// slots or two MXFP8 slots (three workgroups per CU).
+template <int kFmt, bool kGateUp, bool kSmall>
+struct Ring {
+  static constexpr bool kMx = kFmt == MOE_W_MXFP8;
+  static constexpr int kSub = kSmall ? 1 : kMaxSub;
+  static constexpr int kABytes = 2 * kTileRows * (kMx ? kSlabK : kSlabK / 2);
+  static constexpr int kPages = kGateUp ? 0 : 1;
+  static constexpr int kSlotMax = kABytes + (kSub * kSteps + kPages) * 1024;
+  static constexpr int kBytes =
+      kSmall ? (kMx ? 2 : 3) * kSlotMax : (2 * kSlotMax > 64 * 1024 ? 2 * kSlotMax : 64 * 1024);
+};
 
 // One workgroup of eight waves computes a tile of 2 x 64 weight rows against
 // one aligned block: wave w takes row set w / 4 (gate/up: the gate rows or
 // the up rows of 64 neurons; down: rows 0..63 or 64..127 of a 128-row tile),
 // rows 16 (w % 4) .. +15 of it.
-// kGateUp: epilogue silu(gate) * up (else yhat rows). kPlanes: B planes (1: x;
-// 2: the hi and lo planes). kSteps: 32-element MFMA steps per slab (4 or 2).
-// kFlush: steps per scaled partial (g / 32, at most kSteps). kRing: LDS ring
-// bytes (kRingBytes, or a small ring for blocks of one sub-tile, where the
-// kernel is held to 80 VGPRs so that three workgroups share a CU).
-template <int kFmt, bool kGateUp, int kPlanes, int kSteps, int kFlush, int kRing>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kRing == kRingBytes ? 1 : 6)))
+// kGateUp: bf16 products and the silu(gate) * up epilogue (else fp16
+// products and yhat rows). kFlush: steps per scaled partial (g / 32, at most
+// kSteps). kSmall: blocks of one sub-tile (b <= 16, which the launch
+// guarantees), a small ring and an 80-VGPR budget so that three workgroups
+// share a CU.
+template <int kFmt, bool kGateUp, int kFlush, bool kSmall>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kSmall ? 6 : 1)))
 void grouped_gemm(const GemmParams p) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
-  // Sub-tiles a block can have: four (b <= 64), or one with the small ring
-  // (b <= 16, which the launch guarantees).
-  constexpr int kSub = kRing == kRingBytes ? kMaxSub : 1;
-  constexpr int kSlabK = 32 * kSteps;                  // reduction elements per slab
+  constexpr bool kHalf = !kGateUp;                     // fp16 operands
+  constexpr int kSub = Ring<kFmt, kGateUp, kSmall>::kSub;
+  constexpr int kRing = Ring<kFmt, kGateUp, kSmall>::kBytes;
   constexpr int kRowBytes = kMx ? kSlabK : kSlabK / 2; // weight bytes per row and slab
   constexpr int kRowsPerDma = 1024 / kRowBytes;        // weight rows per 1 KB LDS-DMA
   constexpr int kABytes = 2 * kTileRows * kRowBytes;   // weight bytes per slab (128 rows)
@@ -177,10 +251,11 @@ void grouped_gemm(const GemmParams p) {
   static_assert(kADma == 4 || kADma == 8 || kADma == 16, "weight DMAs per slab");
   // The pipeline keeps at least two slots in flight at the largest slot (every
   // sub-tile active); the depth computed per task relies on it.
-  static_assert(kRing >= 2 * (kABytes + kSub * kPlanes * kSteps * 1024), "ring holds two slabs");
+  static_assert(kRing >= 2 * Ring<kFmt, kGateUp, kSmall>::kSlotMax, "ring holds two slabs");
+  static_assert(kABytes == Ring<kFmt, kGateUp, kSmall>::kABytes, "weight bytes per slab");
   __shared__ __align__(16) unsigned char ring[kRing];
   __shared__ __align__(16) unsigned char ssh[2 * kScStride];
-  __shared__ __align__(16) unsigned char szz[2 * kZpStride];
+  __shared__ __align__(16) unsigned char szz[kMx ? 16 : 2 * kZpStride];
   __shared__ int cols[kMaxTok];    // route of each block column, -1 for padding
   __shared__ int brow[kMaxTok];    // B row of each column (0 for padding)
 
@@ -195,7 +270,7 @@ void grouped_gemm(const GemmParams p) {
   const int row_bytes = kMx ? p.K : p.K / 2, gpr = p.K / p.g;
   constexpr int kScBytes = kMx ? 1 : 2;                 // E8M0 byte or fp16 scale
   const int nslab = p.K / kSlabK;
-  const uint32_t nib_mask = in_vgpr(0x000F000Fu);
+  const uint32_t nib_mask = in_vgpr(kNibMask<kHalf>);
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
     const int blk = task / p.ntile;
@@ -247,9 +322,12 @@ void grouped_gemm(const GemmParams p) {
       }
     }
     // Ring geometry: one slot per slab holds the 128 weight rows, then the
-    // activations of every (plane, active sub-tile, step), 1 KB each.
-    const int nbdma = nact * kPlanes * kSteps;                 // activation DMAs per slab
-    const int slot_bytes = kABytes + nbdma * 1024;
+    // activations of every (active sub-tile, step), 1 KB each, then (down)
+    // the page of chunk multipliers.
+    constexpr int kPages = Ring<kFmt, kGateUp, kSmall>::kPages;
+    const int nbdma = nact * kSteps;                           // activation DMAs per slab
+    const int page_off = kABytes + nbdma * 1024;               // multiplier page within a slot
+    const int slot_bytes = page_off + kPages * 1024;
     const int depth_fit = kRing / slot_bytes;
     const int depth = depth_fit < kMaxDepth ? depth_fit : kMaxDepth;   // >= 2 (static_assert above)
     // This wave's DMAs per slab: weight DMA i goes to wave i, activation DMA
@@ -258,7 +336,10 @@ void grouped_gemm(const GemmParams p) {
     // Weight DMA m goes to wave m % 8 (kADma is 4, 8 or 16).
     constexpr int kAMax = (kADma + kGemmWaves - 1) / kGemmWaves;   // weight DMAs per wave, at most
     const int my_a = kADma >= kGemmWaves ? kADma / kGemmWaves : (wave < kADma ? 1 : 0);
-    const int per_slab = my_b + my_a;
+    // The multiplier page goes to the last wave (it has no more activation
+    // DMAs than any other).
+    const bool my_page = kPages > 0 && wave == kGemmWaves - 1;
+    const int per_slab = my_b + my_a + (my_page ? 1 : 0);
 
     // Everything before this point is a plain load the compiler waits for;
     // from here on the only vector-memory operations are the LDS-DMA loads
@@ -298,8 +379,8 @@ void grouped_gemm(const GemmParams p) {
       qa[t] = p.q + grow * row_bytes + 16 * ch;
     }
     // This wave's activation DMAs (at most two per slab: nbdma <= 16):
-    // DMA i = ((plane * nact + u) * kSteps + j) is issued by wave i % 8 and
-    // reads step j of this lane's column in active sub-tile u.
+    // DMA i = (u * kSteps + j) is issued by wave i % 8 and reads step j of
+    // this lane's column in active sub-tile u.
     const uint16_t* bsrc[2] = {p.b0, p.b0};
     int boff[2] = {0, 0};
 #pragma unroll
@@ -307,14 +388,21 @@ void grouped_gemm(const GemmParams p) {
       const int i = wave + kGemmWaves * t;
       if (i >= nbdma) continue;
       const int j = i % kSteps;
-      const int pu = i / kSteps;
-      const int pl = (kPlanes == 2 && pu >= nact) ? 1 : 0;
-      int m = amask;                      // the (pu - pl * nact)-th active sub-tile
-      for (int v = pu - pl * nact; v > 0; --v) m &= m - 1;
+      int m = amask;                      // the (i / kSteps)-th active sub-tile
+      for (int v = i / kSteps; v > 0; --v) m &= m - 1;
       const int st = __builtin_ctz(m);
-      const uint16_t* base = pl ? p.b1 : p.b0;
-      bsrc[t] = base + static_cast<size_t>(brow[16 * st + n]) * p.K + 32 * j + 8 * lq;
+      bsrc[t] = p.b0 + static_cast<size_t>(brow[16 * st + n]) * p.K + 32 * j + 8 * lq;
       boff[t] = kABytes + i * 1024;
+    }
+    // Multiplier page (down): lane 16 u + c reads the 16-byte entry of column
+    // c of active sub-tile u for the slab (lanes past the active sub-tiles
+    // read row 0's and are not used).
+    const float* pnext = p.bsc;
+    if (my_page) {
+      int m = amask;
+      for (int v = lane >> 4; v > 0 && m != 0; --v) m &= m - 1;
+      const int row = m != 0 ? brow[16 * __builtin_ctz(m) + n] : 0;
+      pnext = p.bsc + static_cast<size_t>(row) * (p.K / kSlabK) * 4;
     }
     // Ring slots are walked with running offsets, and the DMA sources with
     // running pointers: no divisions in the slab loop.
@@ -333,8 +421,10 @@ void grouped_gemm(const GemmParams p) {
         if (t < my_a) dma16(anext[t], lds_addr(slot + (wave + kGemmWaves * t) * 1024));
         anext[t] += kRowBytes;
       }
+      if (my_page) dma16(pnext, lds_addr(slot + page_off));
       bnext0 += kSlabK;
       bnext1 += kSlabK;
+      pnext += 4;
     };
 
     floatx4 acc[kSub];            // per active index u (sub-tile act[u])
@@ -392,47 +482,60 @@ void grouped_gemm(const GemmParams p) {
 #pragma unroll
       for (int f = 0; f < kSteps / kFlush; ++f) {
         const int grp = grp0 + f;
-        bf16x8 Z;
+        uint4 Z;
         float cs[4];
         if constexpr (kMx) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) cs[i] = e8m0_to_float(sp[i * gpr + grp]);
         } else {
-          Z = neg_zero_pairs(zpl[grp]);
+          Z = neg_zero_pairs<kHalf>(zpl[grp]);
           const uint16_t* sp16 = reinterpret_cast<const uint16_t*>(sp);
 #pragma unroll
           for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(sp16[i * gpr + grp]);
         }
-        bf16x8 A[kFlush];
+        uint4 A[kFlush];
 #pragma unroll
         for (int jj = 0; jj < kFlush; ++jj) {
           if constexpr (kMx) {
             const uint32_t* w = aw[kFlush * f + jj];
-            A[jj] = __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
-                                                          fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])));
+            A[jj] = fp8_operand<kHalf>(w[0], w[1]);
           } else {
-            A[jj] = bias_pairs(aw[kFlush * f + jj][0], nib_mask);
+            A[jj] = bias_pairs<kHalf>(aw[kFlush * f + jj][0], nib_mask);
           }
         }
+        // Down: the intermediate's scaling is uniform over 64-element chunks
+        // (two steps), so a partial spans at most one chunk.
+        constexpr int kPart = (kHalf && kFlush > 2) ? 2 : kFlush;
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
-          // One chain per active sub-tile: the bias product and the
-          // zero-point product accumulate into the same partial.
-          floatx4 d = {0, 0, 0, 0};
-#pragma unroll
-          for (int jj = 0; jj < kFlush; ++jj) {
-            const int j = kFlush * f + jj;
-#pragma unroll
-            for (int pl = 0; pl < kPlanes; ++pl) {
-              const bf16x8 B = __builtin_bit_cast(
-                  bf16x8, *reinterpret_cast<const uint4*>(slot + kABytes + (((pl * nact + u) * kSteps + j) * 1024) + 16 * lane));
-              d = mfma_bf16(A[jj], B, d);
-              if constexpr (!kMx) d = mfma_bf16(Z, B, d);
-            }
+          float pm[2] = {1.0f, 1.0f};
+          if constexpr (kHalf) {
+            const float2 v = *reinterpret_cast<const float2*>(slot + page_off + 16 * (16 * u + n));
+            pm[0] = v.x;
+            pm[1] = v.y;
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(cs[i], d[i], acc[u][i]);
+          for (int h = 0; h < kFlush / kPart; ++h) {
+            // One chain per active sub-tile and partial: the bias product and
+            // the zero-point product accumulate into the same partial.
+            floatx4 d = {0, 0, 0, 0};
+#pragma unroll
+            for (int jj = h * kPart; jj < (h + 1) * kPart; ++jj) {
+              const int j = kFlush * f + jj;
+              const uint4 B = *reinterpret_cast<const uint4*>(slot + kABytes + (u * kSteps + j) * 1024 + 16 * lane);
+              d = mfma16<kHalf>(A[jj], B, d);
+              if constexpr (!kMx) d = mfma16<kHalf>(Z, B, d);
+            }
+            if constexpr (kHalf) {
+              const float m = pm[(kFlush * f + h * kPart) / 2];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(cs[i] * m, d[i], acc[u][i]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(cs[i], d[i], acc[u][i]);
+            }
+          }
           // Keep this sub-tile's accumulation in its own iteration: the
           // compiler can otherwise merge the accumulations into one tail that
           // the loop exit jumps into right after an MFMA whose result it
@@ -458,27 +561,44 @@ void grouped_gemm(const GemmParams p) {
           *reinterpret_cast<floatx4*>(xch + (((wave & 3) * kSub + u) * kWave + lane) * 4) = acc[u];
       }
       lds_barrier();
+      // Gate waves: a = silu(gate) * up in place, and each column's largest
+      // |a| over this wave's 16 neurons (lane groups combined by two
+      // exchanges) into LDS beside the hand-off area.
+      float* xmax = xch + 4 * kSub * kWave * 4;    // [gate wave][active index][column]
+      if (rs == 0) {
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+          if (u >= nact) break;
+          const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kSub + u) * kWave + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[u][i] = silu_mul(acc[u][i], up[i]);
+          float m = fmaxf(fmaxf(fabsf(acc[u][0]), fabsf(acc[u][1])), fmaxf(fabsf(acc[u][2]), fabsf(acc[u][3])));
+          m = fmaxf(m, __shfl_xor(m, 16, kWave));
+          m = fmaxf(m, __shfl_xor(m, 32, kWave));
+          if (lq == 0) xmax[(wave * kSub + u) * 16 + n] = m;
+        }
+      }
+      lds_barrier();
+      // Each valid column's 64 neurons are scaled by 2^t (the largest
+      // magnitude into [2^14, 2^15)) and written as fp16; the gate wave of
+      // the first 16 neurons stores 2^-t in the column's chunk entry.
       if (rs == 0) {
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
           const int r = cols[16 * act[u] + n];
           if (r < 0) continue;
-          const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kSub + u) * kWave + lane) * 4);
-          uint32_t hi2[2], lo2[2];
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const float v0 = silu_mul(acc[u][i], up[i]);
-            const float v1 = silu_mul(acc[u][i + 1], up[i + 1]);
-            const bf16x2 h = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
-            const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-            const bf16x2 l = {static_cast<__bf16>(v0 - bf16_lo(hb)), static_cast<__bf16>(v1 - bf16_hi(hb))};
-            hi2[i / 2] = hb;
-            lo2[i / 2] = __builtin_bit_cast(uint32_t, l);
-          }
+          const float m = fmaxf(fmaxf(xmax[u * 16 + n], xmax[(kSub + u) * 16 + n]),
+                                fmaxf(xmax[(2 * kSub + u) * 16 + n], xmax[(3 * kSub + u) * 16 + n]));
+          const int t = chunk_shift(m);
+          const float sup = pow2f(t);
+          const halfx2 h01 = {static_cast<_Float16>(acc[u][0] * sup), static_cast<_Float16>(acc[u][1] * sup)};
+          const halfx2 h23 = {static_cast<_Float16>(acc[u][2] * sup), static_cast<_Float16>(acc[u][3] * sup)};
           const size_t off = static_cast<size_t>(r) * p.out_rows + ng * p.tile_stride + rl + 4 * lq;
-          *reinterpret_cast<uint2*>(p.a_hi + off) = make_uint2(hi2[0], hi2[1]);
-          *reinterpret_cast<uint2*>(p.a_lo + off) = make_uint2(lo2[0], lo2[1]);
+          *reinterpret_cast<uint2*>(p.a16 + off) =
+              make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+          if (wave == 0 && lq == 0)
+            p.a_scale[(static_cast<size_t>(r) * (p.out_rows / kSlabK) + (ng >> 1)) * 4 + (ng & 1)] = pow2f(-t);
         }
       }
     } else {
@@ -549,74 +669,64 @@ bool group_ok(int K, int g, int slab) {
   return g < slab ? (slab % g) == 0 : (g % slab) == 0;
 }
 
-template <int kFmt, bool kGateUp, int kPlanes, int kSteps, int kRing>
+template <int kFmt, bool kGateUp, bool kSmall>
 hipError_t launch_gemm_ring(const GemmParams& gp, int wgs, hipStream_t stream) {
   if constexpr (kFmt == MOE_W_MXFP8) {
-    hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 1, kRing>), dim3(wgs), dim3(kGemmThreads), 0,
-                       stream, gp);
-    return hipGetLastError();
-  }
-  switch (flush_steps(gp.g, kSteps)) {
-    case 1:
-      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 1, kRing>), dim3(wgs), dim3(kGemmThreads), 0,
-                         stream, gp);
-      break;
-    case 2:
-      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, 2, kRing>), dim3(wgs), dim3(kGemmThreads), 0,
-                         stream, gp);
-      break;
-    default:
-      hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kPlanes, kSteps, kSteps, kRing>), dim3(wgs),
-                         dim3(kGemmThreads), 0, stream, gp);
-      break;
+    hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, 1, kSmall>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+  } else {
+    switch (flush_steps(gp.g, kSteps)) {
+      case 1:
+        hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, 1, kSmall>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+        break;
+      case 2:
+        hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, 2, kSmall>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+        break;
+      default:
+        hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kSteps, kSmall>), dim3(wgs), dim3(kGemmThreads), 0,
+                           stream, gp);
+        break;
+    }
   }
   return hipGetLastError();
 }
 
 // MXFP8 blocks are 32 elements: one scaled partial per MFMA step. Layers
 // aligned with b <= 16 have one 16-column sub-tile per block, whose ring
-// slots are small: a 36 KB ring (int4; 40 KB for MXFP8's wider weight rows)
-// keeps two or more slots in flight and lets three workgroups share a CU
-// (more tasks per round).
-template <bool kGateUp, int kPlanes, int kSteps>
+// slots are small: the small ring keeps two or more slots in flight and lets
+// three workgroups share a CU (more tasks per round).
+template <bool kGateUp>
 hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t stream) {
   if (fmt == MOE_W_MXFP8) {
-    if (gp.b <= 16)
-      return launch_gemm_ring<MOE_W_MXFP8, kGateUp, kPlanes, kSteps, kSmallRingMxBytes>(gp, wgs, stream);
-    return launch_gemm_ring<MOE_W_MXFP8, kGateUp, kPlanes, kSteps, kRingBytes>(gp, wgs, stream);
+    if (gp.b <= 16) return launch_gemm_ring<MOE_W_MXFP8, kGateUp, true>(gp, wgs, stream);
+    return launch_gemm_ring<MOE_W_MXFP8, kGateUp, false>(gp, wgs, stream);
   }
-  if (gp.b <= 16) return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, kPlanes, kSteps, kSmallRingBytes>(gp, wgs, stream);
-  return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, kPlanes, kSteps, kRingBytes>(gp, wgs, stream);
+  if (gp.b <= 16) return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, true>(gp, wgs, stream);
+  return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, false>(gp, wgs, stream);
 }
-
-constexpr int kGateUpSteps = 4;   // 128-element slabs
-constexpr int kDownSteps = 2;     // 64-element slabs (two planes of activations)
 
 }  // namespace
 
 bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2) {
   // Whole slabs and whole tiles in both GEMMs (gate/up: 64 neurons; down:
-  // 128 rows); the tile's scales (and int4 zeros) are staged in LDS: int4 at
-  // most 32 groups per row, MXFP8 at most 64 blocks of 32 per row.
-  if (b < 1 || b > kMaxTok || (H % 128) != 0 || (I % 64) != 0 || (H % (32 * kGateUpSteps)) != 0 ||
-      (I % (32 * kDownSteps)) != 0)
-    return false;
+  // 128 rows; 128-element slabs); the tile's scales (and int4 zeros) are
+  // staged in LDS: int4 at most 32 groups per row, MXFP8 at most 64 blocks
+  // of 32 per row.
+  if (b < 1 || b > kMaxTok || (H % kSlabK) != 0 || (I % kSlabK) != 0) return false;
   if (fmt == MOE_W_MXFP8) return g13 == 32 && g2 == 32 && H / 32 <= 2 * kMaxGpr && I / 32 <= 2 * kMaxGpr;
-  return group_ok(H, g13, 32 * kGateUpSteps) && group_ok(I, g2, 32 * kDownSteps);
+  return group_ok(H, g13, kSlabK) && group_ok(I, g2, kSlabK);
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   GemmParams gp{};
   gp.b0 = p.x;
-  gp.b1 = nullptr;
   gp.sorted = p.sorted;
   gp.blocks = p.blocks;
   gp.num_padded = p.num_padded;
   gp.q = static_cast<const unsigned char*>(p.w13.q);
   gp.sc = static_cast<const unsigned char*>(p.w13.scale);
   gp.zp = p.w13.zero;
-  gp.a_hi = p.a_hi;
-  gp.a_lo = p.a_lo;
+  gp.a16 = p.a16;
+  gp.a_scale = p.a_scale;
   gp.mk = p.M * p.k;
   gp.k = p.k;
   gp.E = p.E;
@@ -630,13 +740,13 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.K = p.H;
   gp.g = p.w13.group;
   const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
-  return launch_gemm<true, 1, kGateUpSteps>(p.w13.fmt, gp, wgs, stream);
+  return launch_gemm<true>(p.w13.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   GemmParams gp{};
-  gp.b0 = p.a_hi;
-  gp.b1 = p.a_lo;
+  gp.b0 = p.a16;
+  gp.bsc = p.a_scale;
   gp.sorted = p.sorted;
   gp.blocks = p.blocks;
   gp.num_padded = p.num_padded;
@@ -657,7 +767,7 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.K = p.I;
   gp.g = p.w2.group;
   const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
-  return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
+  return launch_gemm<false>(p.w2.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream) {
@@ -669,8 +779,8 @@ hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* c
   gp.q = static_cast<const unsigned char*>(p.w13.q);
   gp.sc = static_cast<const unsigned char*>(p.w13.scale);
   gp.zp = p.w13.zero;
-  gp.a_hi = p.a_hi;
-  gp.a_lo = p.a_lo;
+  gp.a16 = p.a16;
+  gp.a_scale = p.a_scale;
   gp.mk = p.E * cap;
   gp.k = 1;
   gp.E = p.E;
@@ -684,13 +794,13 @@ hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* c
   gp.K = p.H;
   gp.g = p.w13.group;
   const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
-  return launch_gemm<true, 1, kGateUpSteps>(p.w13.fmt, gp, wgs, stream);
+  return launch_gemm<true>(p.w13.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream) {
   GemmParams gp{};
-  gp.b0 = p.a_hi;
-  gp.b1 = p.a_lo;
+  gp.b0 = p.a16;
+  gp.bsc = p.a_scale;
   gp.counts = counts;
   gp.cap = cap;
   gp.nbpe = (cap + p.b - 1) / p.b;
@@ -711,7 +821,7 @@ hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* coun
   gp.K = p.I;
   gp.g = p.w2.group;
   const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
-  return launch_gemm<false, 2, kDownSteps>(p.w2.fmt, gp, wgs, stream);
+  return launch_gemm<false>(p.w2.fmt, gp, wgs, stream);
 }
 
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream) {

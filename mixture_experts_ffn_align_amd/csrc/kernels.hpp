@@ -57,8 +57,8 @@ struct GroupedArgs {
   const int32_t* blocks;
   const int32_t* num_padded;
   moe_weights w13, w2;
-  uint16_t* a_hi;  // bf16 [M*k][I]
-  uint16_t* a_lo;  // bf16 [M*k][I]
+  uint16_t* a16;   // fp16 [M*k][I] intermediate, each 64-neuron chunk of a route scaled by a power of two
+  float* a_scale;  // fp32 [M*k][I/128][4]: entries 0 and 1 undo the scaling of the slab's two chunks
   float* yhat;     // fp32 [M*k][H]
   float* y;        // fp32 [M][H]
   int M, H, I, E, k, b;
@@ -72,10 +72,10 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream);
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream);
 
 // The two grouped GEMMs on the fixed-capacity batched layout: expert e's rows
-// are e * cap .. e * cap + counts[e] - 1 of x / the intermediate planes / yhat
-// (counts on the device, clamped to [0, cap]); rows past the count are not
-// read or written. Uses x, w13, w2, a_hi, a_lo, yhat, H, I, E, b and
-// max_workgroups of p.
+// are e * cap .. e * cap + counts[e] - 1 of x / the intermediate (a16 and
+// a_scale) / yhat (counts on the device, clamped to [0, cap]); rows past the
+// count are not read or written. Uses x, w13, w2, a16, a_scale, yhat, H, I,
+// E, b and max_workgroups of p.
 hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream);
 hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* counts, int cap, hipStream_t stream);
 

@@ -15,6 +15,26 @@ import numpy as np
 REL_L2_TOL = 1e-3
 MAX_ABS_REL_RMS = 1e-2
 
+# Bounds for the intermediate a = silu(gate)*up as the library stores it
+# (moe_ffn_intermediate): format 1 (bf16 hi + lo) is within 2^-17 relative of
+# the kernel's fp32 value; format 2 (fp16 scaled per 64-element chunk) within
+# 2^-11, fp16's unit roundoff. Both add the fp32 accumulation error (about
+# 1e-5 at most on these layers).
+INTERMEDIATE_REL_L2 = {1: 1e-4, 2: 2.0 ** -11 + 1e-5}
+
+
+def decode_scaled_f16(a16, mult):
+    """Format-2 intermediate as fp64: a16 [..., I] fp16 values and mult
+    [..., I/128, 4] fp32, entries 0 and 1 of slab s multiplying the elements
+    of chunks 2s and 2s+1 (64 elements each)."""
+    # Rows the library leaves unspecified (invalid routes) and the unused
+    # entries may hold any bits, signalling NaNs included.
+    with np.errstate(invalid="ignore"):
+        a = np.asarray(a16).astype(np.float64)
+        m = np.asarray(mult)[..., :2].astype(np.float64)
+        m = m.reshape(m.shape[:-2] + (a.shape[-1] // 64,))
+        return a * np.repeat(m, 64, axis=-1)
+
 
 def alignment_mismatch(got, ref):
     """None if (sorted, blocks, num_padded) are identical, else a reason."""

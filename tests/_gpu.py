@@ -7,6 +7,7 @@ import torch
 import mixture_experts_ffn_align_amd as moe
 import oracle
 from mixture_experts_ffn_align_amd import DeviceProjection, MoeLayer
+from tests._checks import decode_scaled_f16
 from workloads import make_workload
 
 DEV = "cuda"
@@ -41,19 +42,24 @@ class DeviceWorkload:
         return y
 
     def intermediate(self, path):
-        """Route-indexed silu(gate)*up the last forward left in the workspace (fp64)."""
+        """(route-indexed silu(gate)*up the last forward left in the workspace
+        as fp64, its format)."""
         d = self.layer.desc(self.x.shape[0], path)
         ws = self.layer.workspace(d)
-        off, lo, fmt = moe.moe_ffn_intermediate(d)
+        off, aux, fmt = moe.moe_ffn_intermediate(d)
         mk = self.x.shape[0] * self.cfg.k
-        n = mk * self.cfg.I
-        if fmt == 0:
-            a = ws[off:off + 4 * n].view(torch.float32).double()
-        else:
+        I = self.cfg.I
+        n = mk * I
+        if fmt == 1:
             hi = ws[off:off + 2 * n].view(torch.bfloat16).double()
-            low = ws[lo:lo + 2 * n].view(torch.bfloat16).double()
-            a = hi + low
-        return a.reshape(mk, self.cfg.I).cpu().numpy()
+            low = ws[aux:aux + 2 * n].view(torch.bfloat16).double()
+            a = (hi + low).reshape(mk, I).cpu().numpy()
+        else:
+            assert fmt == 2, fmt
+            a16 = ws[off:off + 2 * n].view(torch.float16).reshape(mk, I).cpu().numpy()
+            mult = ws[aux:aux + 16 * mk * (I // 128)].view(torch.float32).reshape(mk, I // 128, 4).cpu().numpy()
+            a = decode_scaled_f16(a16, mult)
+        return a, fmt
 
 
 @functools.lru_cache(maxsize=8)

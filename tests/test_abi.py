@@ -98,10 +98,10 @@ def test_workspace_size_decode_and_grouped():
     dg = _desc(M=256, b=64)
     assert moe.moe_ffn_kernel_count(dg) == 4
     cap = oracle.align_capacity(256, 8, 128, 64)
-    need = cap * 4 + (cap // 64) * 4 + 2048 * 768 * 2 * 2 + 2048 * 2048 * 4
+    need = cap * 4 + (cap // 64) * 4 + 2048 * 768 * 2 + 2048 * (768 // 128) * 16 + 2048 * 2048 * 4
     assert moe.moe_ffn_workspace_size(dg) >= need
-    off, lo, fmt = moe.moe_ffn_intermediate(dg)
-    assert fmt == 1 and lo > off
+    off, aux, fmt = moe.moe_ffn_intermediate(dg)
+    assert fmt == 2 and aux >= off + 2048 * 768 * 2
     off, lo, fmt = moe.moe_ffn_intermediate(d)
     assert fmt == 1 and lo >= off + 8 * 768 * 2
     assert [moe.moe_ffn_kernel_name(dg, i) for i in range(4)] == [
@@ -125,6 +125,8 @@ def test_auto_path_threshold():
     assert rp(_desc(M=1, k=20)) == B.MOE_PATH_GROUPED              # decode: at most 16 routes per token
     assert rp(_desc(M=1, g13=256, g2=256, I=768, H=2048)) == B.MOE_PATH_DECODE
     assert rp(_desc(M=1, k=20, path=B.MOE_PATH_DECODE)) == -1
+    assert rp(_desc(M=64, I=448, g2=64)) == B.MOE_PATH_DECODE      # grouped: I a multiple of 128
+    assert rp(_desc(M=64, I=448, g2=64, path=B.MOE_PATH_GROUPED)) == -1
     assert rp(_desc(M=-1)) == -1
 
 
