@@ -136,6 +136,17 @@ __device__ __forceinline__ int chunk_shift(float m) {
 
 __device__ __forceinline__ float pow2f(int t) { return __uint_as_float(static_cast<uint32_t>(t + 127) << 23); }
 
+// Largest v over the four lanes of a wave that share l % 16 (one per 16-lane
+// row), in each of them: gfx950's lane swaps across row pairs, no LDS.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);   // rows 0,1 <-> 2,3
+  const float m = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const uint32_t c = __float_as_uint(m);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);   // rows 0,2 <-> 1,3
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
 // LDS byte address of a __shared__ object (low half of its generic address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -562,8 +573,7 @@ void grouped_gemm(const GemmParams p) {
       }
       lds_barrier();
       // Gate waves: a = silu(gate) * up in place, and each column's largest
-      // |a| over this wave's 16 neurons (lane groups combined by two
-      // exchanges) into LDS beside the hand-off area.
+      // |a| over this wave's 16 neurons into LDS beside the hand-off area.
       float* xmax = xch + 4 * kSub * kWave * 4;    // [gate wave][active index][column]
       if (rs == 0) {
 #pragma unroll
@@ -572,9 +582,8 @@ void grouped_gemm(const GemmParams p) {
           const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kSub + u) * kWave + lane) * 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[u][i] = silu_mul(acc[u][i], up[i]);
-          float m = fmaxf(fmaxf(fabsf(acc[u][0]), fabsf(acc[u][1])), fmaxf(fabsf(acc[u][2]), fabsf(acc[u][3])));
-          m = fmaxf(m, __shfl_xor(m, 16, kWave));
-          m = fmaxf(m, __shfl_xor(m, 32, kWave));
+          const float m = max_over_rows(
+              fmaxf(fmaxf(fabsf(acc[u][0]), fabsf(acc[u][1])), fmaxf(fabsf(acc[u][2]), fabsf(acc[u][3]))));
           if (lq == 0) xmax[(wave * kSub + u) * 16 + n] = m;
         }
       }
