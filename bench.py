@@ -355,7 +355,7 @@ def grouped_sweep(fmt):
                              "hbm_frac": round(G * per / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                              "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)})
                 log(json.dumps(rows[-1]))
-            del xb, hi, lo, yb
+            del xb, a16, asc, yb
         del layers
         torch.cuda.empty_cache()
     print(json.dumps({"grouped_sweep": fmt, "shapes": "Qwen3-30B-A3B H=2048 I=768", "rows": rows}), flush=True)
