@@ -267,8 +267,6 @@ void grouped_gemm(const GemmParams p) {
   __shared__ __align__(16) unsigned char ring[kRing];
   __shared__ __align__(16) unsigned char ssh[2 * kScStride];
   __shared__ __align__(16) unsigned char szz[kMx ? 16 : 2 * kZpStride];
-  __shared__ int cols[kMaxTok];    // route of each block column, -1 for padding
-  __shared__ int brow[kMaxTok];    // B row of each column (0 for padding)
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
@@ -286,7 +284,12 @@ void grouped_gemm(const GemmParams p) {
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
     const int blk = task / p.ntile;
     const int ng = task - blk * p.ntile;
-    int e, nrows;    // the block's expert and, in the batched layout, its valid rows
+    // Every wave holds the block's columns itself, lane c column c (b <= 64):
+    // rc is its route (batched layout: its row), -1 for padding, and bc the
+    // B row it reads. The expert ID and the routes are loaded together, and
+    // the active sub-tiles, B rows and output rows come from ballots and
+    // lane reads, with no LDS round trip or barrier before the first DMA.
+    int e, rc = -1;
     if (batched) {
       // Block j of expert e covers rows e * cap + j * b .. +b-1 of the batched
       // operands; rows at or past the expert's count are padding.
@@ -294,33 +297,23 @@ void grouped_gemm(const GemmParams p) {
       const int j = blk - e * p.nbpe;
       const int cnt = min(max(p.counts[e], 0), p.cap);
       if (j * p.b >= cnt) continue;
-      nrows = min(p.b, cnt - j * p.b);
+      if (lane < min(p.b, cnt - j * p.b)) rc = e * p.cap + j * p.b + lane;
     } else {
       if (blk * p.b >= npad) continue;
+      // blk < nblk keeps the index inside the alignment's capacity.
+      const int rr = lane < p.b ? p.sorted[static_cast<size_t>(blk) * p.b + lane] : -1;
       e = p.blocks[blk];
       if (e < 0 || e >= p.E) continue;
-      nrows = p.b;
+      rc = (rr >= 0 && rr < p.mk) ? rr : -1;
     }
-
-    if (threadIdx.x < kMaxTok) {
-      const int c = threadIdx.x;
-      int r = -1;
-      if (batched) {
-        if (c < nrows) r = (blk / p.nbpe) * p.cap + (blk % p.nbpe) * p.b + c;
-      } else if (c < p.b) {
-        r = p.sorted[static_cast<size_t>(blk) * p.b + c];
-        if (r < 0 || r >= p.mk) r = -1;
-      }
-      cols[c] = r;
-      brow[c] = r < 0 ? 0 : ((kGateUp && !batched) ? r / p.k : r);
-    }
-    __syncthreads();
+    const int bc = rc < 0 ? 0 : ((kGateUp && !batched) ? rc / p.k : rc);
     // Active sub-tiles (wave-uniform), listed in order; static indices only,
     // so the lists stay in registers.
+    const uint64_t valid = __ballot(rc >= 0);
     int amask = 0;
 #pragma unroll
     for (int st = 0; st < kSub; ++st) {
-      if (__ballot(cols[16 * st + n] >= 0) != 0ull) amask |= 1 << st;
+      if (((valid >> (16 * st)) & 0xFFFFull) != 0ull) amask |= 1 << st;
     }
     const int nact = __builtin_popcount(amask);
     int act[kSub];                    // sub-tile of each active index
@@ -352,9 +345,10 @@ void grouped_gemm(const GemmParams p) {
     const bool my_page = kPages > 0 && wave == kGemmWaves - 1;
     const int per_slab = my_b + my_a + (my_page ? 1 : 0);
 
-    // Everything before this point is a plain load the compiler waits for;
-    // from here on the only vector-memory operations are the LDS-DMA loads
-    // below (and the epilogue stores after the slab loop).
+    // Everything before this point is a plain load the compiler waits for
+    // (or a store of the previous task's epilogue); from here on the only
+    // vector-memory operations are the LDS-DMA loads below (and the epilogue
+    // stores after the slab loop).
     wait_vm<0>();
 
     const size_t ebase = static_cast<size_t>(e) * p.rows_per_expert + static_cast<size_t>(ng) * p.tile_stride;
@@ -402,7 +396,7 @@ void grouped_gemm(const GemmParams p) {
       int m = amask;                      // the (i / kSteps)-th active sub-tile
       for (int v = i / kSteps; v > 0; --v) m &= m - 1;
       const int st = __builtin_ctz(m);
-      bsrc[t] = p.b0 + static_cast<size_t>(brow[16 * st + n]) * p.K + 32 * j + 8 * lq;
+      bsrc[t] = p.b0 + static_cast<size_t>(__shfl(bc, 16 * st + n, kWave)) * p.K + 32 * j + 8 * lq;
       boff[t] = kABytes + i * 1024;
     }
     // Multiplier page (down): lane 16 u + c reads the 16-byte entry of column
@@ -412,7 +406,8 @@ void grouped_gemm(const GemmParams p) {
     if (my_page) {
       int m = amask;
       for (int v = lane >> 4; v > 0 && m != 0; --v) m &= m - 1;
-      const int row = m != 0 ? brow[16 * __builtin_ctz(m) + n] : 0;
+      const int row_src = __shfl(bc, m != 0 ? 16 * __builtin_ctz(m) + n : n, kWave);
+      const int row = m != 0 ? row_src : 0;
       pnext = p.bsc + static_cast<size_t>(row) * (p.K / kSlabK) * 4;
     }
     // Ring slots are walked with running offsets, and the DMA sources with
@@ -595,7 +590,7 @@ void grouped_gemm(const GemmParams p) {
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
-          const int r = cols[16 * act[u] + n];
+          const int r = __shfl(rc, 16 * act[u] + n, kWave);
           if (r < 0) continue;
           const float m = fmaxf(fmaxf(xmax[u * 16 + n], xmax[(kSub + u) * 16 + n]),
                                 fmaxf(xmax[(2 * kSub + u) * 16 + n], xmax[(3 * kSub + u) * 16 + n]));
@@ -614,13 +609,15 @@ void grouped_gemm(const GemmParams p) {
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
         if (u >= nact) break;
-        const int r = cols[16 * act[u] + n];
+        const int r = __shfl(rc, 16 * act[u] + n, kWave);
         if (r < 0) continue;
         const size_t off = static_cast<size_t>(r) * p.out_rows + ng * p.tile_stride + 64 * rs + rl + 4 * lq;
         *reinterpret_cast<float4*>(p.yhat + off) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
       }
     }
-    __syncthreads();   // cols, brow and the ring are reused by the next task
+    // The ring is reused by the next task. LDS only: the epilogue's global
+    // stores need not land first (the next task's first wait covers them).
+    lds_barrier();
   }
 }
 
