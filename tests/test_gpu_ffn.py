@@ -187,3 +187,27 @@ def test_auto_path_falls_back_to_decode():
     g.announce("ffn-auto-fallback-decode")
     y = dw.forward(moe.MOE_PATH_AUTO).cpu().numpy()
     assert ffn_mismatch(y, ref) is None, ffn_errors(y, ref)
+
+
+@pytest.mark.parametrize("factor", [2.0 ** 10, 2.0 ** -12], ids=["large", "small"])
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_intermediate_beyond_fp16_range(factor, path):
+    # Group scales 2^10 larger push silu(gate)*up far past fp16's largest
+    # finite value (and silu of very negative gates to zero, so chunks mix
+    # zeros with huge values); 2^-12 smaller put every value below fp16's
+    # smallest normal. Both paths must still meet the layer's bar and the
+    # intermediate its format's bound: the grouped path's per-chunk power of
+    # two keeps fp16 within 2^-11 of each value at either end.
+    g = _gpu()
+    wl = _custom(15, M=24, H=256, I=256, E=8, k=2, b=16, g=64, s_lo=0.005 * factor, s_hi=0.02 * factor)
+    ref = oracle.ffn_stages(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
+    a = np.abs(ref["a"])
+    if factor > 1:
+        assert (a > 65504).mean() > 0.25        # the premise: fp16 alone would overflow
+    else:
+        assert a.max() < 2.0 ** -14             # the premise: fp16 alone would be subnormal
+    dw = g.DeviceWorkload(wl)
+    g.announce("ffn-range", factor, path)
+    y = dw.forward(PATHS[path]).cpu().numpy()
+    assert ffn_mismatch(y, ref["y"]) is None, ffn_errors(y, ref["y"])
+    _check_intermediate(dw, ref, PATHS[path])
