@@ -60,6 +60,26 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Sums over the 64 lanes of four values at once, the same bits in every lane
+// of a 16-lane row: gfx950's lane swaps fold the four values into one
+// register, one per 16-lane row (a: row 0, c: row 1, b: row 2, d: row 3),
+// then a DPP butterfly finishes each row. Per value the order is
+// ((l0 + l2) + (l1 + l3)) over the four rows' lanes, then the butterfly.
+__device__ __forceinline__ float wave_sum4_dpp(float a, float b, float c, float d) {
+  const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(d), false, false);
+  // Lanes 0..31: a's rows 0,1 + rows 2,3; lanes 32..63 the same for b.
+  const float sab = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
+  const float scd = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
+  const auto m = __builtin_amdgcn_permlane16_swap(__float_as_uint(sab), __float_as_uint(scd), false, false);
+  float v = __uint_as_float(m[0]) + __uint_as_float(m[1]);   // rows: a, c, b, d
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 // One 32-element chunk of a weight row dotted with 16 bf16 activation pairs
 // (xw). int4: 16 bytes, bf16 (128 + q) pairs, the caller removes the bias
 // and zero point; MXFP8: 32 bytes of E4M3 codes, converted exactly to bf16
@@ -191,12 +211,25 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
         }
       }
     }
+    float gv, uv;
+    if constexpr (kNpw == 2) {
+      // Rows of the folded sums: gate 0, up 0, gate 1, up 1.
+      const float v = wave_sum4_dpp(acc[0], acc[1], acc[2], acc[3]);
+      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+      const float u0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+      const float u1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+      gv = lane == 0 ? g0 : g1;
+      uv = lane == 0 ? u0 : u1;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2 * kNpw; ++j) acc[j] = wave_sum_dpp(acc[j]);
-    float gv = acc[0], uv = acc[kNpw];
+      for (int j = 0; j < 2 * kNpw; ++j) acc[j] = wave_sum_dpp(acc[j]);
+      gv = acc[0];
+      uv = acc[kNpw];
 #pragma unroll
-    for (int j = 1; j < kNpw; ++j) {
-      if (lane == j) { gv = acc[j]; uv = acc[kNpw + j]; }
+      for (int j = 1; j < kNpw; ++j) {
+        if (lane == j) { gv = acc[j]; uv = acc[kNpw + j]; }
+      }
     }
     if (lane < kNpw) {
       const float v = silu_mul(gv, uv);
