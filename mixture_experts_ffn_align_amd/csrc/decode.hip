@@ -375,6 +375,26 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     // Sum each row over the lanes of its slot: DPP butterflies inside 16-lane
     // rows, then (slots wider than 16 lanes) the row sums read out in lane
     // order. Fixed order, no LDS round trips.
+    if constexpr (kSpan == 32 && kRps == 4) {
+      // Two 32-lane slots, four rows each (slot s, index i: row s + 2i). A
+      // lane swap of 16-lane rows adds each slot's two halves and packs four
+      // rows into one register (16-lane rows: rows 0, 2, 1, 3 of a pair of
+      // indices), so two butterflies finish all eight rows.
+      const auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0]), __float_as_uint(acc[1]), false, false);
+      const auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[2]), __float_as_uint(acc[3]), false, false);
+      float v01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+      float v23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+      v01 += dpp<0xB1>(v01);  v23 += dpp<0xB1>(v23);
+      v01 += dpp<0x4E>(v01);  v23 += dpp<0x4E>(v23);
+      v01 += dpp<0x141>(v01); v23 += dpp<0x141>(v23);
+      v01 += dpp<0x140>(v01); v23 += dpp<0x140>(v23);
+      if ((lane & 15) == 0) {
+        const int q = lane >> 4;
+        const int row = (q >> 1) | ((q & 1) << 1);
+        part[wave][row] = v01;
+        part[wave][row + 4] = v23;
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < kRps; ++i) {
       float v = acc[i];
@@ -403,6 +423,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
           if (lane == 0) part[wave][sl + i * kSlots] = v;
         }
       }
+    }
     }
     __syncthreads();
     if (threadIdx.x < kDownRows) {
