@@ -394,6 +394,17 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
         part[wave][row] = v01;
         part[wave][row + 4] = v23;
       }
+    } else if constexpr (kSpan == 64 && kRps == 8) {
+      // One 64-lane slot, eight rows: each group of four accumulators folds
+      // into one register (16-lane rows: rows 0, 2, 1, 3 of the group).
+      const float v0 = wave_sum4_dpp(acc[0], acc[1], acc[2], acc[3]);
+      const float v1 = wave_sum4_dpp(acc[4], acc[5], acc[6], acc[7]);
+      if ((lane & 15) == 0) {
+        const int q = lane >> 4;
+        const int row = (q >> 1) | ((q & 1) << 1);
+        part[wave][row] = v0;
+        part[wave][row + 4] = v1;
+      }
     } else {
 #pragma unroll
     for (int i = 0; i < kRps; ++i) {
