@@ -77,6 +77,37 @@ def test_route_order_within_expert_does_not_change_bytes(name):
     assert outs[0] == digest(dw.forward(moe.MOE_PATH_GROUPED).cpu().numpy())
 
 
+@pytest.mark.parametrize("name", ["batch_m21", "batch_m256_zipf"])
+def test_blocks_without_routes_change_no_byte(name):
+    # A caller-supplied alignment may hold blocks whose rows are all
+    # padding (sentinel route IDs) under a valid expert: one such block
+    # after the first real block and two at the end. Such blocks write
+    # nothing, so the output bytes equal the plain grouped forward's.
+    g = _gpu()
+    dw = g.device_workload(name)
+    cfg = dw.cfg
+    s, blocks, n = oracle.align(dw.wl.topk_ids, cfg.E, cfg.b)
+    mk = cfg.M * cfg.k
+    nb = n // cfg.b
+    pad = np.full(cfg.b, mk, dtype=np.int32)
+    s2 = np.concatenate([s[:cfg.b], pad, s[cfg.b:n], pad, pad]).astype(np.int32)
+    b2 = np.concatenate([blocks[:1], [blocks[0]], blocks[1:nb], [blocks[nb - 1], 0]]).astype(np.int32)
+    n2 = n + 3 * cfg.b
+    assert s2.size == n2 and b2.size == n2 // cfg.b
+    # Tails up to a capacity the entry point accepts (sentinels, -1 blocks).
+    cap = max(moe.moe_align_capacity(cfg.M, cfg.k, cfg.E, cfg.b), n2)
+    s2 = np.concatenate([s2, np.full(cap - n2, mk, dtype=np.int32)])
+    b2 = np.concatenate([b2, np.full(cap // cfg.b - b2.size, -1, dtype=np.int32)])
+    d = dw.layer.desc(cfg.M, moe.MOE_PATH_GROUPED)
+    ws = dw.layer.workspace(d)
+    y = torch.empty((cfg.M, cfg.H), dtype=torch.float32, device="cuda")
+    g.announce("empty-blocks", name)
+    moe.moe_ffn_forward_aligned(d, dw.x, dw.ids, dw.w, torch.from_numpy(s2).cuda(), torch.from_numpy(b2).cuda(),
+                                torch.tensor([n2], dtype=torch.int32, device="cuda"), y, ws)
+    torch.cuda.synchronize()
+    assert digest(y.cpu().numpy()) == digest(dw.forward(moe.MOE_PATH_GROUPED).cpu().numpy())
+
+
 @pytest.mark.parametrize("name,path", CASES[1:])
 def test_token_permutation_permutes_rows_bitwise(name, path):
     g = _gpu()
