@@ -364,7 +364,7 @@ def grouped_sweep(fmt):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the layer is measured on one GPU; sharding across GPUs is a design, not run here: use --gpus 1"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
