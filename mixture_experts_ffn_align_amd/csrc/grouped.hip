@@ -19,10 +19,13 @@
 // lane group q: elements 32j+8q .. 32j+8q+7 of the slab), so every step lies
 // inside one quantisation group whenever g is a multiple of 32.
 //
-// Data movement: the tile's weight rows and the block's activation rows
-// (16 bytes per lane, per active sub-tile and step) go global -> LDS with
-// 16-byte LDS-DMA loads into one ring of slab-sized slots, issued depth - 1
-// slabs ahead; nothing passes through VGPRs. The depth follows from the slot
+// Data movement: the tile's weight rows and the block's activation rows go
+// global -> LDS with 16-byte LDS-DMA loads into one ring of slab-sized slots,
+// issued depth - 1 slabs ahead; nothing passes through VGPRs. An activation
+// DMA fills 1 KB with eight columns times two steps (128 contiguous bytes,
+// one cache line, per column; half the lines of a column-per-lane layout),
+// its 16-byte pieces placed with an XOR of the column so that the MFMA's
+// 16-byte LDS reads of a step stay free of bank conflicts. The depth follows from the slot
 // size (the slot holds only active sub-tiles). Each slab costs one wait on
 // the wave's own loads (an exact vmcnt: the loads of the later slabs stay in
 // flight) and one LDS-only workgroup barrier. Weight and activation loads
@@ -396,7 +399,12 @@ void grouped_gemm(const GemmParams p) {
       int m = amask;                      // the (i / kSteps)-th active sub-tile
       for (int v = i / kSteps; v > 0; --v) m &= m - 1;
       const int st = __builtin_ctz(m);
-      bsrc[t] = p.b0 + static_cast<size_t>(__shfl(bc, 16 * st + n, kWave)) * p.K + 32 * j + 8 * lq;
+      // DMA j of a sub-tile: columns 8 (j & 1) .. +7, steps 2 (j >> 1) and
+      // +1, 128 contiguous bytes per column; lane L takes column L / 8 of the
+      // half and 16-byte piece (L % 8) ^ (column / 2) of its 128 bytes.
+      const int c = 8 * (j & 1) + (lane >> 3);
+      const int pc = (lane & 7) ^ (c >> 1);
+      bsrc[t] = p.b0 + static_cast<size_t>(__shfl(bc, 16 * st + c, kWave)) * p.K + 64 * (j >> 1) + 8 * pc;
       boff[t] = kABytes + i * 1024;
     }
     // Multiplier page (down): lane 16 u + c reads the 16-byte entry of column
@@ -451,6 +459,11 @@ void grouped_gemm(const GemmParams p) {
     const unsigned char* zpl = szz + rs * kZpStride + (rl + n) * gpr;
     // Group of the first partial of a slab: slab s covers groups s * gps ..
     // (g below the slab) or group s / spg (g a multiple of the slab).
+    // B operand of step j for lane (n, lq): column n, piece 4 (j & 1) + lq
+    // of DMA 2 (j >> 1) + n / 8, stored at lane 8 (n % 8) + (piece ^ n / 2).
+    static_assert(kSteps == 4, "two 128-byte column halves per slab");
+    const int boff_b0 = (n >> 3) * 1024 + 16 * (8 * (n & 7) + (lq ^ (n >> 1)));
+    const int boff_b1 = (n >> 3) * 1024 + 16 * (8 * (n & 7) + ((4 + lq) ^ (n >> 1)));
     const int gps = p.g < kSlabK ? kSlabK / p.g : 1;
     const int spg = p.g < kSlabK ? 1 : p.g / kSlabK;
 
@@ -529,7 +542,8 @@ void grouped_gemm(const GemmParams p) {
 #pragma unroll
             for (int jj = h * kPart; jj < (h + 1) * kPart; ++jj) {
               const int j = kFlush * f + jj;
-              const uint4 B = *reinterpret_cast<const uint4*>(slot + kABytes + (u * kSteps + j) * 1024 + 16 * lane);
+              const uint4 B = *reinterpret_cast<const uint4*>(slot + kABytes + (u * kSteps + 2 * (j >> 1)) * 1024 +
+                                                              ((j & 1) ? boff_b1 : boff_b0));
               d = mfma16<kHalf>(A[jj], B, d);
               if constexpr (!kMx) d = mfma16<kHalf>(Z, B, d);
             }
