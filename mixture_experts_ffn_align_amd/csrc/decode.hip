@@ -169,11 +169,16 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
     for (int j = 0; j < 2 * kNpw; ++j) acc[j] = 0.0f;
     const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
     for (int c = lane; c < nch; c += kWave) {
-      // Issue the weight loads first so they are all in flight together.
+      // Loads return in issue order, so the activations and the small scale
+      // and zero loads go first and the four weight rows last: row j's sums
+      // then wait only for row j's weights, and the rows before it are
+      // computed while the later ones land.
+      uint4 xv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xv[v] = xrow[c * 4 + v];
+      __builtin_amdgcn_sched_barrier(0);
       ChunkRow<kFmt> wv[2 * kNpw];
       const int grp = (c << 5) >> g_shift;
-#pragma unroll
-      for (int j = 0; j < 2 * kNpw; ++j) load_chunk<kFmt>(qrow[j], c, wv[j]);
       uint32_t sv[2 * kNpw], zv[2 * kNpw];
 #pragma unroll
       for (int j = 0; j < 2 * kNpw; ++j) {
@@ -184,9 +189,9 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
           zv[j] = zrow[j][grp];
         }
       }
-      uint4 xv[4];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) xv[v] = xrow[c * 4 + v];
+      for (int j = 0; j < 2 * kNpw; ++j) load_chunk<kFmt>(qrow[j], c, wv[j]);
       // Keep every load above this point: the scheduler would otherwise sink
       // some of them below the first use of the others and add a round trip.
       __builtin_amdgcn_sched_barrier(0);
