@@ -205,15 +205,21 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
         for (int j = 0; j < 2 * kNpw; ++j)
           acc[j] = fmaf(e8m0_to_float(sv[j]), dot_chunk<kFmt>(wv[j], xw, nib_mask, 0.0f), acc[j]);
       } else {
+        // The activation sum and the per-row scale terms need only the loads
+        // that land first; they are done before the first weight row's wait.
         float sx = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) sx = dot2_bf16(xw[v], 0x3F803F80u, sx);  // (1.0, 1.0)
+        float s[2 * kNpw], zb[2 * kNpw];
 #pragma unroll
         for (int j = 0; j < 2 * kNpw; ++j) {
-          const float s = half_bits_to_float(static_cast<uint16_t>(sv[j]));
-          const float zb = 128.0f + static_cast<float>(zv[j]);
-          acc[j] = fmaf(s, fmaf(-zb, sx, dot_chunk<kFmt>(wv[j], xw, nib_mask, 0.0f)), acc[j]);
+          s[j] = half_bits_to_float(static_cast<uint16_t>(sv[j]));
+          zb[j] = 128.0f + static_cast<float>(zv[j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 2 * kNpw; ++j)
+          acc[j] = fmaf(s[j], fmaf(-zb[j], sx, dot_chunk<kFmt>(wv[j], xw, nib_mask, 0.0f)), acc[j]);
       }
     }
     float gv, uv;
