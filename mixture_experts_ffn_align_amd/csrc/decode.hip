@@ -144,15 +144,28 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
   for (int task = wave_id; task < ntasks; task += nwaves) {
     const int r = task / tasks_per_route;
     const int i0 = (task - r * tasks_per_route) * kNpw;
+    // The activations do not depend on the expert: their first chunk is
+    // requested before the expert-ID load is waited for.
+    const int t = r / k;
+    const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
+    uint4 xv[4];
+    {
+      const int cx = lane < nch ? lane : 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xv[v] = xrow[cx * 4 + v];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const int e = uniform(load_expert(ids, r, E, ebase));
     if (e < 0) {
+      // A use of the activations on this (rare) side too, so that their
+      // loads stay above the branch instead of being sunk below the ID wait.
+      asm volatile("" ::"v"(xv[0].x));
       if (lane < kNpw) {
         a_hi[static_cast<size_t>(r) * I + i0 + lane] = 0;
         a_lo[static_cast<size_t>(r) * I + i0 + lane] = 0;
       }
       continue;
     }
-    const int t = r / k;
     const size_t row0 = static_cast<size_t>(e) * (2 * I) + i0;  // first gate row
     const unsigned char* qrow[2 * kNpw];
     const unsigned char* srow[2 * kNpw];
@@ -167,15 +180,15 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
     float acc[2 * kNpw];
 #pragma unroll
     for (int j = 0; j < 2 * kNpw; ++j) acc[j] = 0.0f;
-    const uint4* xrow = reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H);
     for (int c = lane; c < nch; c += kWave) {
       // Loads return in issue order, so the activations and the small scale
       // and zero loads go first and the four weight rows last: row j's sums
       // then wait only for row j's weights, and the rows before it are
       // computed while the later ones land.
-      uint4 xv[4];
+      if (c != lane) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) xv[v] = xrow[c * 4 + v];
+        for (int v = 0; v < 4; ++v) xv[v] = xrow[c * 4 + v];
+      }
       __builtin_amdgcn_sched_barrier(0);
       ChunkRow<kFmt> wv[2 * kNpw];
       const int grp = (c << 5) >> g_shift;
