@@ -109,6 +109,10 @@ typedef struct {
 } moe_ffn_desc;
 
 /* Number of int32 entries sorted_route_ids needs: roundup(M*k + min(E, M*k)*(b-1), b).
+ * The alignment ("Route-Block Membership Selects Packed-AWQ Arithmetic", first
+ * paragraph) pads each expert's count to a multiple of b, so every expert that
+ * holds a route adds at most b - 1 padding rows, and at most min(E, M*k) experts
+ * hold one; the page gives no buffer size, and this bound is the plainest one.
  * expert_block_ids needs capacity / b entries. Host-only and pure; returns 0 when
  * M < 0, k < 1, E < 1 or b < 1. */
 MOE_API size_t moe_align_capacity(int32_t M, int32_t k, int32_t E, int32_t b);
@@ -153,8 +157,14 @@ MOE_API moe_status moe_align_ex(const int32_t* topk_ids, int32_t M, int32_t k, i
 MOE_API moe_status moe_align_ex_workspace_size(int32_t M, int32_t k, int32_t E, size_t* bytes);
 
 /* Bytes of device workspace moe_ffn_forward needs for this description (path
- * resolved as moe_ffn_forward resolves it). Errors as moe_ffn_forward's
- * validation. */
+ * resolved as moe_ffn_forward resolves it). The workspace holds what the layer
+ * keeps on the device between its steps: the alignment outputs (grouped path;
+ * counts stay device-resident as in "Hardware-Native Joint Sparse-Quantization
+ * for Trillion-Scale MoE", App. D.1, so no host synchronisation sizes anything),
+ * the route-indexed activation silu(gate)*up and, on the grouped path, the
+ * routed-W2 rows yhat: the intermediate surfaces that "Route-Block Membership
+ * Selects Packed-AWQ Arithmetic" captures (the paragraph on the sparse native
+ * differences). Errors as moe_ffn_forward's validation. */
 MOE_API moe_status moe_ffn_workspace_size(const moe_ffn_desc* d, size_t* bytes);
 
 /* Steps (1)-(4): y = sum_j w[t,j] * W2[e] (silu(W13g[e] x_t) * W13u[e] x_t).
@@ -176,8 +186,11 @@ MOE_API moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, con
 
 /* Grouped path (whatever d->path says) on a caller-supplied alignment (same
  * layout and meaning as moe_align's outputs, with the given capacity). Lets a
- * caller reorder routes within an expert's rows: the output bytes must not
- * change. Route entries
+ * caller reorder routes within an expert's rows: "Route-Block Membership
+ * Selects Packed-AWQ Arithmetic" (the A_e / B(e,j) paragraph, and the paragraph
+ * on reordering routes 22 and 28 inside block 40) states that swapping two
+ * valid routes inside one B(e,j) leaves the computation's identity unchanged;
+ * here the output bytes must not change for any order within an expert. Route entries
  * outside [0, M*k) are padding; blocks whose expert is outside [0, E) are skipped.
  * Each valid route must appear at most once. The workspace must be sized with
  * d->path = MOE_PATH_GROUPED. Errors as moe_ffn_forward. */
@@ -260,6 +273,17 @@ MOE_API const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
 MOE_API moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* aux_offset,
                                 int32_t* format);
 
+/* Where a grouped-path forward call leaves the routed-W2 rows
+ * yhat_r = W2[e] a_r (before the router weight) inside the workspace: fp32
+ * [M*k][H] at *offset, each valid route's row written once by the down GEMM
+ * and read by the combine. Rows of invalid routes are unspecified. This is the
+ * "routed-W2" surface of "Route-Block Membership Selects Packed-AWQ
+ * Arithmetic" (the paragraph on the sparse native differences), which tells a
+ * down-projection error apart from a combine error. The decode path folds the
+ * combine into the down projection's accumulator and keeps no such rows:
+ * MOE_ERR_UNSUPPORTED. Other errors as moe_ffn_forward's validation. */
+MOE_API moe_status moe_ffn_route_outputs(const moe_ffn_desc* d, size_t* offset);
+
 /* Largest M for which MOE_PATH_AUTO picks the decode path. */
 MOE_API int32_t moe_ffn_auto_decode_max_m(void);
 
@@ -267,7 +291,12 @@ MOE_API int32_t moe_ffn_auto_decode_max_m(void);
  * resolved), or -1 when the description is rejected. Host-only. */
 MOE_API int32_t moe_ffn_resolved_path(const moe_ffn_desc* d);
 
-/* Static string for a status code. */
+/* Static string for a status code. Status codes report host-checkable
+ * argument errors only: data-dependent conditions stay on the device (token
+ * counts are device-resident in "Hardware-Native Joint Sparse-Quantization for
+ * Trillion-Scale MoE", App. D.1), so an expert ID outside the experts held here
+ * is a skipped route ("valid routes" in "Route-Block Membership Selects
+ * Packed-AWQ Arithmetic", first paragraph), never an error. */
 MOE_API const char* moe_status_str(moe_status s);
 
 #ifdef __cplusplus

@@ -78,6 +78,7 @@ _SIGNATURES = {
     "moe_ffn_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(moe_ffn_desc), _c_i32]),
     "moe_ffn_intermediate": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size),
                                       ctypes.POINTER(_c_size), ctypes.POINTER(_c_i32)]),
+    "moe_ffn_route_outputs": (_c_i32, [ctypes.POINTER(moe_ffn_desc), ctypes.POINTER(_c_size)]),
     "moe_ffn_auto_decode_max_m": (_c_i32, []),
     "moe_ffn_resolved_path": (_c_i32, [ctypes.POINTER(moe_ffn_desc)]),
     "moe_status_str": (ctypes.c_char_p, [_c_i32]),
@@ -128,6 +129,51 @@ def _stream(stream) -> int | None:
         import torch
         return torch.cuda.current_stream().cuda_stream
     return getattr(stream, "cuda_stream", stream)
+
+
+def _expect(name, t, dtype, shape, device=None):
+    """Check that tensor ``t`` is a contiguous ``dtype`` tensor of ``shape`` on a
+    GPU (on ``device`` when given) before its pointer goes to the library: the
+    kernels read raw memory, so a wrong dtype or a short buffer would misread
+    or run past its end instead of failing."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    return t.device
+
+
+def _check_layer_io(desc, x=None, topk_ids=None, topk_w=None, y=None, ws=None):
+    """dtype / shape checks of a layer call's tensors against ``desc``, then
+    the device checks (all on one GPU)."""
+    import torch
+    M, H, k = desc.M, desc.H, desc.k
+    specs = [("x", x, torch.bfloat16, (M, H)), ("topk_ids", topk_ids, torch.int32, (M, k)),
+             ("topk_w", topk_w, torch.float32, (M, k)), ("y", y, torch.float32, (M, H)),
+             ("ws", ws, torch.uint8, None)]
+    specs = [s for s in specs if s[1] is not None]
+    for name, t, dtype, shape in specs:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    for name, t, dtype, shape in specs:
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+    dev = None
+    for name, t, dtype, shape in specs:
+        dev = _expect(name, t, dtype, tuple(t.shape), dev)
 
 
 # ---------------------------------------------------------------------------
@@ -188,6 +234,7 @@ def moe_ffn_workspace_size(desc: moe_ffn_desc, check: bool = True):
 
 def moe_ffn_forward(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, stream=None,
                     check: bool = True) -> int:
+    _check_layer_io(desc, x, topk_ids, topk_w, y, ws)
     st = lib().moe_ffn_forward(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                _stream(stream))
@@ -199,6 +246,12 @@ def moe_ffn_forward(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, stream=None,
 def moe_ffn_forward_aligned(desc: moe_ffn_desc, x, topk_ids, topk_w, sorted_route_ids,
                             expert_block_ids, num_padded, y, ws, stream=None,
                             check: bool = True) -> int:
+    import torch
+    _check_layer_io(desc, x, topk_ids, topk_w, y, ws)
+    cap = sorted_route_ids.numel()
+    _expect("sorted_route_ids", sorted_route_ids, torch.int32, (cap,), x.device)
+    _expect("expert_block_ids", expert_block_ids, torch.int32, (cap // max(desc.b, 1),), x.device)
+    _expect("num_padded", num_padded, torch.int32, (1,), x.device)
     st = lib().moe_ffn_forward_aligned(
         ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(sorted_route_ids),
         _ptr(expert_block_ids), _ptr(num_padded), sorted_route_ids.numel(), _ptr(y), _ptr(ws),
@@ -212,6 +265,7 @@ def moe_ffn_forward_profiled(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, eve
                              stream=None) -> None:
     """``events`` are torch.cuda.Event(enable_timing=True) objects, one more than
     the kernel count; they are recorded around every kernel on the stream."""
+    _check_layer_io(desc, x, topk_ids, topk_w, y, ws)
     for e in events:
         if int(e.cuda_event) == 0:   # torch creates the HIP event on first record
             e.record()
@@ -223,11 +277,13 @@ def moe_ffn_forward_profiled(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, eve
 
 
 def moe_ffn_gate_up(desc: moe_ffn_desc, x, topk_ids, ws, stream=None) -> None:
+    _check_layer_io(desc, x, topk_ids, None, None, ws)
     _check(lib().moe_ffn_gate_up(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)), "moe_ffn_gate_up")
 
 
 def moe_ffn_down_combine(desc: moe_ffn_desc, topk_ids, topk_w, y, ws, stream=None) -> None:
+    _check_layer_io(desc, None, topk_ids, topk_w, y, ws)
     _check(lib().moe_ffn_down_combine(ctypes.byref(desc), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_ffn_down_combine")
@@ -236,6 +292,12 @@ def moe_ffn_down_combine(desc: moe_ffn_desc, topk_ids, topk_w, y, ws, stream=Non
 def moe_ffn_gate_up_batched(desc: moe_ffn_desc, xb, counts, a16, a_scale, stream=None) -> None:
     """xb [E, capacity, H] bf16, counts [E] int32 (device), a16 [E, capacity, I]
     fp16 and a_scale [E, capacity, I/128, 4] fp32 (intermediate format 2)."""
+    import torch
+    E, cap = desc.E, xb.shape[1] if xb.dim() == 3 else -1
+    dev = _expect("xb", xb, torch.bfloat16, (E, cap, desc.H))
+    _expect("counts", counts, torch.int32, (E,), dev)
+    _expect("a16", a16, torch.float16, (E, cap, desc.I), dev)
+    _expect("a_scale", a_scale, torch.float32, (E, cap, desc.I // 128, 4), dev)
     _check(lib().moe_ffn_gate_up_batched(ctypes.byref(desc), _ptr(xb), _ptr(counts), xb.shape[1],
                                          _ptr(a16), _ptr(a_scale), _stream(stream)),
            "moe_ffn_gate_up_batched")
@@ -244,6 +306,12 @@ def moe_ffn_gate_up_batched(desc: moe_ffn_desc, xb, counts, a16, a_scale, stream
 def moe_ffn_down_batched(desc: moe_ffn_desc, a16, a_scale, counts, yb, stream=None) -> None:
     """a16 [E, capacity, I] fp16 and a_scale [E, capacity, I/128, 4] fp32, counts [E]
     int32, yb [E, capacity, H] fp32."""
+    import torch
+    E, cap = desc.E, a16.shape[1] if a16.dim() == 3 else -1
+    dev = _expect("a16", a16, torch.float16, (E, cap, desc.I))
+    _expect("a_scale", a_scale, torch.float32, (E, cap, desc.I // 128, 4), dev)
+    _expect("counts", counts, torch.int32, (E,), dev)
+    _expect("yb", yb, torch.float32, (E, cap, desc.H), dev)
     _check(lib().moe_ffn_down_batched(ctypes.byref(desc), _ptr(a16), _ptr(a_scale), _ptr(counts),
                                       a16.shape[1], _ptr(yb), _stream(stream)),
            "moe_ffn_down_batched")
@@ -264,6 +332,13 @@ def moe_ffn_intermediate(desc: moe_ffn_desc) -> tuple[int, int, int]:
     _check(lib().moe_ffn_intermediate(ctypes.byref(desc), ctypes.byref(off), ctypes.byref(aux),
                                       ctypes.byref(fmt)), "moe_ffn_intermediate")
     return int(off.value), int(aux.value), int(fmt.value)
+
+
+def moe_ffn_route_outputs(desc: moe_ffn_desc) -> int:
+    """Offset of the grouped path's routed-W2 rows (fp32 [M*k][H]) in the workspace."""
+    off = _c_size(0)
+    _check(lib().moe_ffn_route_outputs(ctypes.byref(desc), ctypes.byref(off)), "moe_ffn_route_outputs")
+    return int(off.value)
 
 
 def moe_ffn_auto_decode_max_m() -> int:

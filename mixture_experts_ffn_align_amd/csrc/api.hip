@@ -435,6 +435,16 @@ moe_status moe_ffn_intermediate(const moe_ffn_desc* d, size_t* offset, size_t* a
   return MOE_OK;
 }
 
+moe_status moe_ffn_route_outputs(const moe_ffn_desc* d, size_t* offset) {
+  if (offset == nullptr) return MOE_ERR_INVALID_ARG;
+  Layout L;
+  const moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (L.path != MOE_PATH_GROUPED) return MOE_ERR_UNSUPPORTED;
+  *offset = L.off_yhat;
+  return MOE_OK;
+}
+
 int32_t moe_ffn_auto_decode_max_m(void) { return kAutoDecodeMaxM; }
 
 int32_t moe_ffn_resolved_path(const moe_ffn_desc* d) {

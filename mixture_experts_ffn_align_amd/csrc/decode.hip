@@ -35,7 +35,7 @@ namespace {
 
 constexpr int kGateUpThreads = 256;
 constexpr int kGateUpWaves = kGateUpThreads / kWave;
-constexpr int kNpw = 2;                       // neurons per wave
+constexpr int kNpw = 2;                       // neurons per wave (the row folding assumes 2)
 constexpr int kDownWaves = 8;
 constexpr int kDownThreads = kDownWaves * kWave;
 constexpr int kDownRows = 8;
@@ -43,21 +43,6 @@ constexpr int kDownRows = 8;
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-
-// Sum over the 64 lanes of a wave, the same bits in every lane: butterflies
-// inside each 16-lane row with DPP (xor 1, xor 2, half-row mirror, row
-// mirror), then the four row sums added as (r0 + r1) + (r2 + r3).
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
 }
 
 // Sums over the 64 lanes of four values at once, the same bits in every lane
@@ -235,26 +220,14 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
           acc[j] = fmaf(s[j], fmaf(-zb[j], sx, dot_chunk<kFmt>(wv[j], xw, nib_mask, 0.0f)), acc[j]);
       }
     }
-    float gv, uv;
-    if constexpr (kNpw == 2) {
-      // Rows of the folded sums: gate 0, up 0, gate 1, up 1.
-      const float v = wave_sum4_dpp(acc[0], acc[1], acc[2], acc[3]);
-      const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-      const float u0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-      const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-      const float u1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-      gv = lane == 0 ? g0 : g1;
-      uv = lane == 0 ? u0 : u1;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2 * kNpw; ++j) acc[j] = wave_sum_dpp(acc[j]);
-      gv = acc[0];
-      uv = acc[kNpw];
-#pragma unroll
-      for (int j = 1; j < kNpw; ++j) {
-        if (lane == j) { gv = acc[j]; uv = acc[kNpw + j]; }
-      }
-    }
+    // Rows of the folded sums: gate 0, up 0, gate 1, up 1.
+    const float v = wave_sum4_dpp(acc[0], acc[1], acc[2], acc[3]);
+    const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float u0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float u1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    const float gv = lane == 0 ? g0 : g1;
+    const float uv = lane == 0 ? u0 : u1;
     if (lane < kNpw) {
       const float v = silu_mul(gv, uv);
       const __bf16 h = static_cast<__bf16>(v);
@@ -285,7 +258,6 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
   const int ntiles = M * tiles_per_tok;
   const int nch = I >> 5, gpr = I >> g_shift;
   const int row_bytes = kMx ? I : I / 2;
-  const int sc_bytes = kMx ? 1 : 2;
   const int span = kSpan, slots = kSlots;
   const int slot = lane / kSpan;
   const int c0 = lane - slot * kSpan;

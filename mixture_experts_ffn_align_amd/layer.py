@@ -80,6 +80,8 @@ class MoeLayer:
                 y: torch.Tensor | None = None, path: int | None = None,
                 max_workgroups: int | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
         M = x.shape[0]
+        if x.device != self.w13.q.device:
+            raise ValueError(f"x is on {x.device}, the weights on {self.w13.q.device}")
         d = self.desc(M, path, max_workgroups)
         if y is None:
             y = torch.empty((M, self.H), dtype=torch.float32, device=x.device)

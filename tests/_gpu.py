@@ -62,6 +62,17 @@ class DeviceWorkload:
         return a, fmt
 
 
+    def route_outputs(self, path):
+        """The grouped path's routed-W2 rows yhat [M*k][H] (fp64) that the last
+        forward left in the workspace."""
+        d = self.layer.desc(self.x.shape[0], path)
+        ws = self.layer.workspace(d)
+        off = moe.moe_ffn_route_outputs(d)
+        mk = self.x.shape[0] * self.cfg.k
+        n = mk * self.cfg.H
+        return ws[off:off + 4 * n].view(torch.float32).reshape(mk, self.cfg.H).double().cpu().numpy()
+
+
 @functools.lru_cache(maxsize=8)
 def device_workload(name, seed=0):
     return DeviceWorkload(make_workload(name, seed=seed))

@@ -144,3 +144,22 @@ def test_w2_scale_doubling_doubles_output_bitwise(name, path):
     alt = g.DeviceWorkload(type(wl)(wl.cfg, wl.seed, wl.x, wl.topk_ids, wl.topk_w, wl.w13, w2))
     y2 = alt.forward(PATHS[path]).cpu().numpy()
     assert digest(y2) == digest(2 * y1)
+
+
+@pytest.mark.parametrize("fmt,g", [("int4", 128), ("mxfp8", 32)])
+@pytest.mark.parametrize("H", [4096, 2080])
+def test_decode_wide_hidden_repeats_and_caps(fmt, g, H):
+    # H / 32 > 64: decode gate/up lanes take a second 32-element chunk of the
+    # activations (every lane at H = 4096, only lane 0 at H = 2080). Repeats
+    # and workgroup caps must leave every output byte unchanged.
+    import dataclasses
+    from workloads import CONFIGS, make_workload
+    gpu = _gpu()
+    cfg = dataclasses.replace(CONFIGS["tiny"], name="wide", M=3, H=H, I=128, E=8, k=2, b=8, g=g, fmt=fmt)
+    dw = gpu.DeviceWorkload(make_workload(cfg, seed=21))
+    gpu.announce("decode-wide", fmt, H)
+    ref = digest(dw.forward(moe.MOE_PATH_DECODE).cpu().numpy())
+    for _ in range(5):
+        assert digest(dw.forward(moe.MOE_PATH_DECODE).cpu().numpy()) == ref
+    for cap in (1, 7, 100):
+        assert digest(dw.forward(moe.MOE_PATH_DECODE, max_workgroups=cap).cpu().numpy()) == ref

@@ -26,11 +26,18 @@ def _gpu():
 
 
 def _check_intermediate(dw, st, path):
+    """The stored activation silu(gate)*up and, on the grouped path, the
+    routed-W2 rows yhat against the oracle's, on the valid routes: a failure is
+    then placed in the gate/up GEMM, the down GEMM or the combine."""
     a, fmt = dw.intermediate(path)
     assert fmt == (1 if path == moe.MOE_PATH_DECODE else 2), fmt
     valid = (dw.wl.topk_ids.reshape(-1) >= 0) & (dw.wl.topk_ids.reshape(-1) < dw.cfg.E)
     err = ffn_errors(a[valid], st["a"][valid])
     assert err["rel_l2"] < INTERMEDIATE_REL_L2[fmt], err
+    if path == moe.MOE_PATH_GROUPED and valid.any():
+        yhat = dw.route_outputs(path)
+        ref = st["yhat"].reshape(-1, dw.cfg.H)
+        assert ffn_mismatch(yhat[valid], ref[valid]) is None, ffn_errors(yhat[valid], ref[valid])
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_m1", "batch_m21", "batch_m256_zipf", "mxfp8_m64"])
@@ -83,6 +90,13 @@ RAGGED = [
     dict(M=3, H=512, I=448, E=16, k=5, b=8, g=32, fmt="mxfp8"),
     dict(M=2, H=384, I=2176, E=16, k=12, b=8, g=32, fmt="mxfp8"),
     dict(M=70, H=1024, I=256, E=16, k=6, b=64, g=32, fmt="mxfp8"),
+    # Decode gate/up with more than one 32-element chunk per lane (H/32 > 64):
+    # a whole second chunk (H = 4096) and one lane with a second chunk
+    # (H = 2080; the grouped path needs H a multiple of 128), both formats.
+    dict(M=2, H=4096, I=256, E=8, k=4, b=8, g=128),
+    dict(M=3, H=2080, I=128, E=8, k=2, b=8, g=32),
+    dict(M=2, H=4096, I=256, E=8, k=4, b=8, g=32, fmt="mxfp8"),
+    dict(M=3, H=2080, I=128, E=8, k=2, b=8, g=32, fmt="mxfp8"),
     # An odd number of 128-element slabs in the down GEMM (three), on both
     # rings and both formats.
     dict(M=24, H=384, I=384, E=16, k=5, b=16, g=128),
