@@ -201,9 +201,14 @@ MOE_API moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t
                                    const int32_t* num_padded, size_t capacity, float* y,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Same as moe_ffn_forward, and records events[0] before the first kernel and
- * events[i+1] after kernel i (n_events must be moe_ffn_kernel_count + 1) so a
- * caller can time each kernel on the stream. Events are caller-created. */
+/* Same as moe_ffn_forward, and records the start and end of kernel i (in
+ * launch order, the kernels moe_ffn_kernel_name lists) into events[2i] and
+ * events[2i + 1] (n_events must be 2 * moe_ffn_kernel_count): the kernel's own
+ * dispatch timestamps (hipExtLaunchKernel), so that hipEventElapsedTime of the
+ * pair is the kernel's duration with no launch gap around it. A kernel made of
+ * several launches (alignment of more than 8192 routes) spans from the first
+ * launch's start to the last one's end. Events are caller-created; not for use
+ * under graph capture. */
 MOE_API moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
                                     const int32_t* topk_ids, const float* topk_w, float* y,
                                     void* ws, size_t ws_bytes, hipStream_t stream,

@@ -85,6 +85,14 @@ _SIGNATURES = {
 }
 
 _lib = None
+_bench_lib = None
+BENCH_LIB_PATH = os.path.join(_PKG, "libmoe_bench.so")
+BENCH_HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_bench.h")
+_BENCH_SIGNATURES = {
+    "moe_bench_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_ptr,
+                                       _c_ptr, _c_ptr]),
+    "moe_bench_copy": (_c_i32, [_c_ptr, _c_ptr, _c_size, _c_i32, _c_ptr, _c_ptr, _c_ptr]),
+}
 
 
 def lib() -> ctypes.CDLL:
@@ -104,11 +112,27 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def declared_symbols() -> list[str]:
-    """Entry points include/moe_ffn.h declares."""
-    with open(HEADER_PATH) as f:
+def bench_lib() -> ctypes.CDLL:
+    """The measurement kernels (include/moe_bench.h); raises if not built."""
+    global _bench_lib
+    if _bench_lib is None:
+        if not os.path.exists(BENCH_LIB_PATH):
+            raise RuntimeError(f"{BENCH_LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_ffn_align_amd.build`")
+        L = ctypes.CDLL(BENCH_LIB_PATH)
+        for name, (res, args) in _BENCH_SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _bench_lib = L
+    return _bench_lib
+
+
+def declared_symbols(header: str = HEADER_PATH, macro: str = "MOE_API") -> list[str]:
+    """Entry points a header declares (include/moe_ffn.h by default)."""
+    with open(header) as f:
         text = f.read()
-    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+    return re.findall(macro + r"\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
 
 
 def status_str(status: int) -> str:
@@ -263,8 +287,8 @@ def moe_ffn_forward_aligned(desc: moe_ffn_desc, x, topk_ids, topk_w, sorted_rout
 
 def moe_ffn_forward_profiled(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, events,
                              stream=None) -> None:
-    """``events`` are torch.cuda.Event(enable_timing=True) objects, one more than
-    the kernel count; they are recorded around every kernel on the stream."""
+    """``events`` are torch.cuda.Event(enable_timing=True) objects, two per
+    kernel: events[2i] and events[2i + 1] take kernel i's start and end."""
     _check_layer_io(desc, x, topk_ids, topk_w, y, ws)
     for e in events:
         if int(e.cuda_event) == 0:   # torch creates the HIP event on first record

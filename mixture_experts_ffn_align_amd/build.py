@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
 SOURCES = ["api.hip", "align.hip", "decode.hip", "grouped.hip"]
+# Measurement kernels (streaming-read floor, copy peak) for bench.py.
+BENCH_LIB = os.path.join(PKG, "libmoe_bench.so")
+BENCH_SOURCES = ["bench_kernels.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -33,21 +36,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into the shared library; returns its path."""
-    tmp = LIB + ".tmp"
+def _compile(sources, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    text = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if out.strip() and verbose:
-        print(out)
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{text}")
+    if text.strip() and verbose:
+        print(text)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the layer library and the measurement library; returns the
+    layer library's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
     return LIB
 
 

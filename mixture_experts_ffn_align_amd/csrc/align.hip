@@ -302,17 +302,17 @@ hipError_t launch_align(const int32_t* ids, int mk, int E, int ebase, int b, int
   const size_t lds = align_lds_bytes(E);
   const size_t need = align_ws_bytes(mk, E);
   if (need == 0 || ws == nullptr || ws_bytes < need) {
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), lds, stream, ids, mk, E, ebase, b, nbits,
+    launch(align_kernel, dim3(1), dim3(kThreads), lds, stream, ids, mk, E, ebase, b, nbits,
                        sorted, blocks, num_padded, cap);
     return hipGetLastError();
   }
   const int G = align_groups(mk);
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* totals = counts + static_cast<size_t>(G) * E;
-  hipLaunchKernelGGL(align_count, dim3(G), dim3(kThreads), sizeof(int) * static_cast<size_t>(E), stream, ids, mk,
+  launch(align_count, dim3(G), dim3(kThreads), sizeof(int) * static_cast<size_t>(E), stream, ids, mk,
                      E, ebase, kAlignRoutesPerGroup, counts);
-  hipLaunchKernelGGL(align_colscan, dim3((E + 255) / 256), dim3(256), 0, stream, counts, G, E, totals);
-  hipLaunchKernelGGL(align_scatter, dim3(G), dim3(kThreads), lds, stream, ids, mk, E, ebase, b, nbits,
+  launch(align_colscan, dim3((E + 255) / 256), dim3(256), 0, stream, counts, G, E, totals);
+  launch(align_scatter, dim3(G), dim3(kThreads), lds, stream, ids, mk, E, ebase, b, nbits,
                      kAlignRoutesPerGroup, counts, totals, sorted, blocks, num_padded, cap);
   return hipGetLastError();
 }

@@ -9,6 +9,15 @@
 #include "kernels.hpp"
 #include "moe_ffn.h"
 
+namespace moe {
+
+LaunchTiming*& launch_timing() {
+  static thread_local LaunchTiming* t = nullptr;
+  return t;
+}
+
+}  // namespace moe
+
 namespace {
 
 constexpr int32_t kMaxExperts = 2048;
@@ -114,6 +123,12 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+int kernel_count_of(const Layout& L, bool aligned_input) {
+  if (L.path == MOE_PATH_DECODE) return 2;
+  return aligned_input ? 3 : 4;
+}
+
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -132,14 +147,29 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
                        const int32_t* ids, const float* w, float* y, void* ws,
                        const int32_t* a_sorted, const int32_t* a_blocks, const int32_t* a_npad,
                        size_t a_cap, hipStream_t s, hipEvent_t* ev) {
+  // Profiled calls: kernel i records its start in ev[2i] and its end in
+  // ev[2i + 1] (see moe::LaunchTiming); the timing is removed on every exit.
   int kidx = 0;
+  moe::LaunchTiming timing{nullptr, nullptr};
+  struct Uninstall {
+    ~Uninstall() { moe::launch_timing() = nullptr; }
+  } uninstall;
+  const int nk = ev == nullptr ? 0 : kernel_count_of(L, a_sorted != nullptr);
+  auto arm = [&](void) {
+    if (ev == nullptr || kidx >= nk) {
+      moe::launch_timing() = nullptr;
+      return;
+    }
+    timing = moe::LaunchTiming{ev[2 * kidx], ev[2 * kidx + 1]};
+    moe::launch_timing() = &timing;
+  };
   auto mark = [&](void) -> moe_status {
-    if (ev != nullptr && hipEventRecord(ev[kidx], s) != hipSuccess) return MOE_ERR_HIP;
     ++kidx;
+    arm();
     return MOE_OK;
   };
+  arm();
   moe_status st;
-  if ((st = mark()) != MOE_OK) return st;
   if (L.path == MOE_PATH_DECODE) {
     moe::DecodeArgs p{};
     p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
@@ -205,11 +235,6 @@ moe_status check_io(const moe_ffn_desc* d, const uint16_t* x, const int32_t* ids
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   (void)d;
   return MOE_OK;
-}
-
-int kernel_count_of(const Layout& L, bool aligned_input) {
-  if (L.path == MOE_PATH_DECODE) return 2;
-  return aligned_input ? 3 : 4;
 }
 
 }  // namespace
@@ -306,7 +331,7 @@ moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,
   if (st != MOE_OK) return st;
   if (d->M == 0) return MOE_OK;
   if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
-  if (events == nullptr || n_events != kernel_count_of(L, false) + 1) return MOE_ERR_INVALID_ARG;
+  if (events == nullptr || n_events != 2 * kernel_count_of(L, false)) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < n_events; ++i)
     if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
   return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,

@@ -450,7 +450,7 @@ int log2_of(int g) {
 
 template <int kFmt, int kCh, int kSpan>
 void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_down<kFmt, kCh, kSpan>), dim3(wgs), dim3(kDownThreads), 0, stream,
+  launch(decode_down<kFmt, kCh, kSpan>, dim3(wgs), dim3(kDownThreads), 0, stream,
                      p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const unsigned char*>(p.w2.q),
                      static_cast<const unsigned char*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E,
                      p.ebase, p.H, p.I, log2_of(p.w2.group));
@@ -489,10 +489,10 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const auto* q = static_cast<const unsigned char*>(p.w13.q);
   const auto* s = static_cast<const unsigned char*>(p.w13.scale);
   if (p.w13.fmt == MOE_W_MXFP8)
-    hipLaunchKernelGGL(decode_gate_up<MOE_W_MXFP8>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q, s,
+    launch(decode_gate_up<MOE_W_MXFP8>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q, s,
                        p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
   else
-    hipLaunchKernelGGL(decode_gate_up<MOE_W_INT4_AWQ>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q,
+    launch(decode_gate_up<MOE_W_INT4_AWQ>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q,
                        s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
   return hipGetLastError();
 }

@@ -692,17 +692,17 @@ bool group_ok(int K, int g, int slab) {
 template <int kFmt, bool kGateUp, bool kSmall>
 hipError_t launch_gemm_ring(const GemmParams& gp, int wgs, hipStream_t stream) {
   if constexpr (kFmt == MOE_W_MXFP8) {
-    hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, 1, kSmall>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+    launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
   } else {
     switch (flush_steps(gp.g, kSteps)) {
       case 1:
-        hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, 1, kSmall>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+        launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
         break;
       case 2:
-        hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, 2, kSmall>), dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+        launch(grouped_gemm<kFmt, kGateUp, 2, kSmall>, dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
         break;
       default:
-        hipLaunchKernelGGL((grouped_gemm<kFmt, kGateUp, kSteps, kSmall>), dim3(wgs), dim3(kGemmThreads), 0,
+        launch(grouped_gemm<kFmt, kGateUp, kSteps, kSmall>, dim3(wgs), dim3(kGemmThreads), 0,
                            stream, gp);
         break;
     }
@@ -847,7 +847,7 @@ hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* coun
 hipError_t launch_combine(const GroupedArgs& p, hipStream_t stream) {
   const int64_t total = int64_t(p.M) * (p.H / 4);
   const int wgs = grid_for((total + kThreads - 1) / kThreads, p.max_workgroups);
-  hipLaunchKernelGGL(combine_topk, dim3(wgs), dim3(kThreads), 0, stream, p.yhat, p.ids, p.topk_w,
+  launch(combine_topk, dim3(wgs), dim3(kThreads), 0, stream, p.yhat, p.ids, p.topk_w,
                      p.y, p.M, p.k, p.E, p.ebase, p.H);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (api.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,29 @@
 #include "moe_ffn.h"
 
 namespace moe {
+
+// Per-kernel timing of moe_ffn_forward_profiled: while a LaunchTiming is
+// installed (one per host thread), every launch records the kernel's own
+// start and end timestamps into these events (hipExtLaunchKernel); the start
+// event is consumed by the first launch of a stage, the end event is
+// re-recorded by each launch, so a stage of several launches spans them all.
+struct LaunchTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchTiming*& launch_timing();
+
+template <typename... KArgs, typename... Args>
+void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds_bytes, hipStream_t stream,
+            Args... args) {
+  LaunchTiming* t = launch_timing();
+  if (t == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+  } else {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, t->start, t->stop, 0, args...);
+    t->start = nullptr;
+  }
+}
 
 // Every kernel strides over its tasks, so its grid may be smaller than its
 // task count; launches are capped at kMaxGrid workgroups (and at a caller's

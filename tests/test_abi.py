@@ -23,6 +23,23 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), f"{n} declared in include/moe_ffn.h but not exported"
 
 
+def test_measurement_library_exports_and_validates():
+    names = B.declared_symbols(B.BENCH_HEADER_PATH, "MOE_BENCH_API")
+    assert set(names) == {"moe_bench_stream_read", "moe_bench_copy"}
+    L = B.bench_lib()
+    for n in names:
+        assert hasattr(L, n)
+    rd, cp = L.moe_bench_stream_read, L.moe_bench_copy
+    assert rd(None, 16, FAKE, 1, 4, None, None, None, None) == 1
+    assert rd(FAKE, 17, FAKE, 1, 4, None, None, None, None) == 1
+    assert rd(FAKE + 4, 16, FAKE, 1, 4, None, None, None, None) == 1
+    assert rd(FAKE, 16, FAKE, 0, 4, None, None, None, None) == 1
+    assert rd(FAKE, 16, FAKE, 1, 3, None, None, None, None) == 1
+    assert cp(FAKE, None, 16, 4, None, None, None) == 1
+    assert cp(FAKE, FAKE + 8, 16, 4, None, None, None) == 1
+    assert cp(FAKE, FAKE, 16, 32, None, None, None) == 1
+
+
 @pytest.mark.parametrize("M,k,E,b", [(4, 2, 8, 8), (1, 8, 128, 8), (21, 8, 128, 8),
                                      (256, 8, 128, 64), (3, 2, 4, 2), (0, 8, 128, 8),
                                      (5, 3, 2, 16), (100, 1, 1, 1)])
@@ -182,7 +199,7 @@ def test_forward_validation_enqueues_nothing():
               None) == B.MOE_ERR_INVALID_ARG
     assert fa(ctypes.byref(dg), FAKE, FAKE, FAKE, None, FAKE, FAKE, cap, FAKE, FAKE, need,
               None) == B.MOE_ERR_INVALID_ARG
-    # profiled variant: event count must be kernel count + 1
+    # profiled variant: two events (start, end) per kernel
     ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
     assert L.moe_ffn_forward_profiled(ctypes.byref(_desc(M=1)), FAKE, FAKE, FAKE, FAKE, FAKE,
                                       10**9, None, ev, 2) == B.MOE_ERR_INVALID_ARG

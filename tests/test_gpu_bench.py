@@ -33,3 +33,37 @@ def test_bench_reports_the_contract_fields():
     assert r["traffic"] is None or r["traffic"] > 0
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
+    # Replay statistics, the measured floors and the warm number.
+    assert d["replays"] >= 10
+    assert d["ms_per_step_p10"] <= d["ms_per_step_median"] <= d["ms_per_step_p90"]
+    assert d["copy_peak_GBps"] > 0 and 0 < d["hbm_frac_vs_floor"]
+    assert d["warm_us_per_layer"] > 0
+    assert r["read_floor_us_same_bytes"] > 0
+
+
+def test_measurement_kernels_read_and_copy_every_byte():
+    # The streaming-read kernel's per-workgroup XORs combine to the XOR of
+    # every word of the buffer, and the copy reproduces the buffer, on a size
+    # with a partial last tile.
+    import numpy as np
+    import torch
+    import ctypes
+    from mixture_experts_ffn_align_amd import _binding as B
+    L = B.bench_lib()
+    n = (3 << 20) + 4096 + 16          # bytes: 192 whole 16 KiB tiles and a ragged tail
+    host = np.random.default_rng(5).integers(0, 2**32, size=n // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    grid = ctypes.c_int32(0)
+    s = torch.cuda.current_stream().cuda_stream
+    want = np.bitwise_xor.reduce(host)
+    for unroll in (1, 2, 4, 8, 16):
+        sink.zero_()
+        assert L.moe_bench_stream_read(src.data_ptr(), n, sink.data_ptr(), sink.numel(), unroll, ctypes.byref(grid),
+                                       None, None, s) == 0
+        dst = torch.zeros_like(src)
+        assert L.moe_bench_copy(src.data_ptr(), dst.data_ptr(), n, unroll, None, None, s) == 0
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink[:grid.value].cpu().numpy().view(np.uint32))
+        assert grid.value == -(-n // (256 * unroll * 16)) and got == want, unroll
+        assert torch.equal(src, dst), unroll

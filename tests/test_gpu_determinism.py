@@ -146,8 +146,8 @@ def test_w2_scale_doubling_doubles_output_bitwise(name, path):
     assert digest(y2) == digest(2 * y1)
 
 
-@pytest.mark.parametrize("fmt,g", [("int4", 128), ("mxfp8", 32)])
-@pytest.mark.parametrize("H", [4096, 2080])
+@pytest.mark.parametrize("fmt,g,H", [("int4", 128, 4096), ("mxfp8", 32, 4096), ("int4", 32, 2080),
+                                     ("mxfp8", 32, 2080)])
 def test_decode_wide_hidden_repeats_and_caps(fmt, g, H):
     # H / 32 > 64: decode gate/up lanes take a second 32-element chunk of the
     # activations (every lane at H = 4096, only lane 0 at H = 2080). Repeats
