@@ -184,6 +184,27 @@ MOE_API moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, con
                            const float* topk_w, float* y, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* moe_ffn_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The library keeps one static device
+ * scratch buffer of moe_ffn_noalloc_max_bytes() bytes (32 MiB) per GPU, held
+ * from the first use on that GPU until the process ends; its address is looked
+ * up once per device. This call allocates nothing, launches the same kernels
+ * as moe_ffn_forward with that buffer as the workspace, and gives the same
+ * output bytes. No part of the scratch needs clearing (every region the layer
+ * reads is written earlier in the same call). Calls that overlap in time on
+ * one GPU share the buffer and race: serialise them (one stream, or events).
+ * The intermediate and yhat of the last call stay in the scratch but are not
+ * exposed.
+ * Errors as moe_ffn_forward, and MOE_ERR_WORKSPACE when the layer needs more
+ * than moe_ffn_noalloc_max_bytes() of workspace (moe_ffn_workspace_size). */
+MOE_API moe_status moe_ffn_forward_noalloc(const moe_ffn_desc* d, const uint16_t* x,
+                                           const int32_t* topk_ids, const float* topk_w, float* y,
+                                           hipStream_t stream);
+
+/* Bytes of the static scratch moe_ffn_forward_noalloc uses per GPU. */
+MOE_API size_t moe_ffn_noalloc_max_bytes(void);
+
 /* Grouped path (whatever d->path says) on a caller-supplied alignment (same
  * layout and meaning as moe_align's outputs, with the given capacity). Lets a
  * caller reorder routes within an expert's rows: "Route-Block Membership

@@ -63,6 +63,9 @@ _SIGNATURES = {
     "moe_ffn_forward_aligned": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr,
                                          _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr, _c_ptr,
                                          _c_size, _c_ptr]),
+    "moe_ffn_forward_noalloc": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                         _c_ptr]),
+    "moe_ffn_noalloc_max_bytes": (_c_size, []),
     "moe_ffn_forward_profiled": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_ptr, _c_size, _c_ptr,
                                           ctypes.POINTER(_c_ptr), _c_i32]),
@@ -265,6 +268,21 @@ def moe_ffn_forward(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, stream=None,
     if check:
         _check(st, "moe_ffn_forward")
     return st
+
+
+def moe_ffn_forward_noalloc(desc: moe_ffn_desc, x, topk_ids, topk_w, y, stream=None,
+                            check: bool = True) -> int:
+    """moe_ffn_forward on the library's static per-GPU scratch (no workspace)."""
+    _check_layer_io(desc, x, topk_ids, topk_w, y)
+    st = lib().moe_ffn_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
+                                       _stream(stream))
+    if check:
+        _check(st, "moe_ffn_forward_noalloc")
+    return st
+
+
+def moe_ffn_noalloc_max_bytes() -> int:
+    return int(lib().moe_ffn_noalloc_max_bytes())
 
 
 def moe_ffn_forward_aligned(desc: moe_ffn_desc, x, topk_ids, topk_w, sorted_route_ids,

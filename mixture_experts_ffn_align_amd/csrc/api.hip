@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "moe_ffn.h"
@@ -237,6 +238,32 @@ moe_status check_io(const moe_ffn_desc* d, const uint16_t* x, const int32_t* ids
   return MOE_OK;
 }
 
+// Device scratch of moe_ffn_forward_noalloc: the workspace of one forward
+// call, for callers that cannot allocate. One copy per GPU, held from the
+// code object's load until the process ends. Its name is a host-side stand-in
+// in host code; the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// The current device's scratch address, looked up on its first use.
+moe_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -299,6 +326,22 @@ moe_status moe_ffn_forward(const moe_ffn_desc* d, const uint16_t* x, const int32
   if (st != MOE_OK) return st;
   if (d->M == 0) return MOE_OK;
   if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
+  return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,
+                     stream, nullptr);
+}
+
+size_t moe_ffn_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+moe_status moe_ffn_forward_noalloc(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                                   const float* topk_w, float* y, hipStream_t stream) {
+  Layout L;
+  moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if (L.total > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != MOE_OK) return st;
+  if ((st = check_io(d, x, topk_ids, topk_w, y, ws, kNoAllocScratchBytes, L)) != MOE_OK) return st;
   return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,
                      stream, nullptr);
 }
