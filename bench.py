@@ -106,8 +106,18 @@ def parse():
                    help="only measure the streaming-read floor and the copy peak and exit")
     p.add_argument("--batch-sweep", action="store_true",
                    help="only run the decode-vs-grouped batch sweep and exit")
+    p.add_argument("--trace-phases", default=None, metavar="KERNEL_TRACE_CSV",
+                   help="only summarise a rocprofv3 kernel trace of a default run of this script (same --steps, "
+                        "--warmup, --replays): per-kernel durations by phase, then exit (no GPU needed)")
+    p.add_argument("--traffic-record", nargs=4, default=None,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="only turn four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE over this "
+                        "script on --workload, then over --copy-calibration) into the traffic record that the "
+                        "roofline's traffic field reads, and exit (no GPU needed)")
     p.add_argument("--grouped-sweep", default=None, metavar="FMT",
                    help="only run the grouped-GEMM shape sweep on the batched layout (int4 or mxfp8) and exit")
+    p.add_argument("--sweep-g", default=None, help="comma-separated expert counts for --grouped-sweep")
+    p.add_argument("--sweep-n", default=None, help="comma-separated token counts for --grouped-sweep")
     return p.parse_args()
 
 
@@ -553,7 +563,7 @@ def rounded(d):
 # Sweeps
 # ---------------------------------------------------------------------------
 
-SWEEP_M = (1, 4, 8, 9, 10, 13, 16, 21, 32, 64)
+SWEEP_M = (1, 4, 8, 9, 10, 12, 13, 14, 15, 16, 21, 32, 64)
 
 
 def batch_sweep(replays):
@@ -606,7 +616,7 @@ SWEEP_N = (16, 32, 64, 128, 256, 512, 1024)
 SWEEP_COLD_BYTES = 640 << 20    # weight copies rotated per point: more than the 256 MB Infinity Cache
 
 
-def grouped_sweep(fmt):
+def grouped_sweep(fmt, gs=None, ns=None):
     """The two grouped GEMMs of a Qwen3-30B-A3B-shaped layer (gate/up: 1536 x
     2048, down: 2048 x 768; H = 2048, I = 768) on the fixed-capacity batched
     layout, over G experts and a maximum of N tokens per expert with the
@@ -626,13 +636,13 @@ def grouped_sweep(fmt):
     per2 = full2.nbytes() / cfg.E
     rng = np.random.default_rng(0)
     rows = []
-    for G in SWEEP_G:
+    for G in (gs or SWEEP_G):
         def take(p):
             return moe.DeviceProjection(p.fmt, p.group, p.q[:G].clone(), p.scale[:G].clone(),
                                         None if p.zero is None else p.zero[:G].clone())
         copies = max(2, int(math.ceil(SWEEP_COLD_BYTES / (G * (per13 + per2)))))
         layers = [moe.MoeLayer(take(full13), take(full2), G, H, I, 1, 64) for _ in range(copies)]
-        for N in SWEEP_N:
+        for N in (ns or SWEEP_N):
             counts_l = [[N, 3 * N // 4, N // 2, N // 4][e % 4] for e in range(G)]
             counts = torch.tensor(counts_l, dtype=torch.int32, device="cuda")
             xv = rng.standard_normal((G, N, H)).astype(np.float32)
@@ -671,10 +681,115 @@ def grouped_sweep(fmt):
     print(json.dumps({"grouped_sweep": fmt, "shapes": "Qwen3-30B-A3B H=2048 I=768", "rows": rows}), flush=True)
 
 
+def trace_phases(path, steps, warmup, replays):
+    """Per-phase durations of the headline workload's two decode kernels in a
+    rocprofv3 kernel trace (CSV) of a default run of this script: the
+    dispatches of each kernel in start order, split by the phases main() runs
+    them in (layer warm-up, untimed and timed layer replays, the single-kernel
+    stage graphs, the dispatch-event pass, the warm graph)."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    kp = min(steps, PROFILE_STEPS)
+    warm = min(steps, WARM_STEPS)
+    out = {}
+    for k, name in enumerate(("decode_gate_up", "decode_down")):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+             if f"::{name}<" in r["Kernel_Name"]]
+        phases = [("layer: eager warm-up", warmup), ("layer: untimed replay", steps),
+                  ("layer: timed replays", replays * steps)]
+        stage = [("stage graph: eager warm-up", 3), ("stage graph: untimed replay", kp),
+                 ("stage graph: timed replays (roofline)", replays * kp)]
+        # The gate/up stage runs before the down stage; each launches only its own kernel.
+        phases += stage
+        phases += [("dispatch events: untimed", kp), ("dispatch events: timed", replays * kp),
+                   ("warm graph", warm + replays * warm)]
+        res, i = [], 0
+        for pn, n in phases:
+            seg = d[i:i + n]
+            i += n
+            if seg:
+                res.append({"phase": pn, "n": len(seg), "mean_us": round(statistics.fmean(seg), 3),
+                            "median_us": round(statistics.median(seg), 3)})
+        out[name] = {"dispatches": len(d), "mean_us": round(statistics.fmean(d), 3), "phases": res,
+                     "unassigned": len(d) - i}
+    print(json.dumps({"trace_phases": path, "kernels": out}), flush=True)
+
+
+def _pmc_means(directory, counter):
+    """Mean counter value (KiB) per dispatch of each kernel in a rocprofv3
+    --pmc output directory (its *counter_collection.csv files)."""
+    import csv
+    import glob
+    sums = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r["Kernel_Name"]
+            s = sums.setdefault(name, [0.0, 0])
+            s[0] += float(r["Counter_Value"])
+            s[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in sums.items()}
+
+
+def traffic_record(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per launch of each kernel of `workload` from FETCH_SIZE and
+    WRITE_SIZE passes, each scaled by what the same counter reads on a plain
+    copy of known size (bench.py --copy-calibration: 64 MiB), written into the
+    traffic record with the hash of the kernels' sources."""
+    from workloads import CONFIGS, make_weights
+    cfg = CONFIGS[workload]
+    copy_bytes = 64 << 20
+    cf = _pmc_means(copy_fetch_dir, "FETCH_SIZE")
+    cw = _pmc_means(copy_write_dir, "WRITE_SIZE")
+    ck = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
+    if not ck:
+        raise SystemExit("no copy kernel in the calibration passes")
+    c_f = max((cf[k] for k in ck), key=lambda v: v[1])[0]
+    c_w = max((cw[k] for k in cw if "copyBuffer" in k or "copy" in k.lower()), key=lambda v: v[1])[0]
+    fetch_factor = copy_bytes / 1024.0 / c_f
+    write_factor = copy_bytes / 1024.0 / c_w
+    w13, w2 = make_weights(cfg, 0, 0)
+    fam = "decode" if cfg.M <= 9 else "grouped"
+    fm = _pmc_means(fetch_dir, "FETCH_SIZE")
+    wm = _pmc_means(write_dir, "WRITE_SIZE")
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {"kernels": {}}
+    rec["calibration"] = {"kernel": "the copy of bench.py --copy-calibration (64 MiB)", "copy_bytes": copy_bytes,
+                          "fetch_size_kib": round(c_f, 2), "write_size_kib": round(c_w, 2),
+                          "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)}
+    for short, alg in (("decode_gate_up", 8 * w13.expert_bytes()), ("decode_down", 8 * w2.expert_bytes())):
+        names = [k for k in fm if f"::{short}<" in k]
+        if not names:
+            continue
+        k = names[0]
+        f_kib, n = fm[k]
+        w_kib = wm.get(k, (0.0, 0))[0]
+        hbm = f_kib * 1024 * fetch_factor + w_kib * 1024 * write_factor
+        rec["kernels"][f"{workload}:{short}"] = {
+            "rocprof_name": k.split("::")[-1].split("(")[0], "dispatches": n,
+            "fetch_size_kib": round(f_kib, 1), "write_size_kib": round(w_kib, 1),
+            "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes": int(alg),
+            "ratio_to_algorithmic": round(hbm / alg, 4), "source_hash": source_hash(fam)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec), flush=True)
+
+
 # ---------------------------------------------------------------------------
 
 def main():
     args = parse()
+    if args.trace_phases:
+        trace_phases(args.trace_phases, args.steps, args.warmup, args.replays)
+        return
+    if args.traffic_record:
+        traffic_record(args.workload, *args.traffic_record)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "the layer is measured on one GPU; sharding across GPUs is a design, "
                                    "not run here: use --gpus 1"}))
@@ -697,7 +812,9 @@ def main():
         batch_sweep(args.replays)
         return
     if args.grouped_sweep:
-        grouped_sweep(args.grouped_sweep)
+        grouped_sweep(args.grouped_sweep,
+                      [int(v) for v in args.sweep_g.split(",")] if args.sweep_g else None,
+                      [int(v) for v in args.sweep_n.split(",")] if args.sweep_n else None)
         return
 
     from workloads import CONFIGS
