@@ -45,6 +45,10 @@ SHAPES = [
     dict(E=8, cap=70, H=2048, I=768, b=64, g=128, counts=None, fmt="int4"),          # {N, 3N/4, N/2, N/4}
     dict(E=5, cap=33, H=512, I=256, b=16, g=32, counts=[33, 1, 16, 17, -4], fmt="int4"),
     dict(E=4, cap=40, H=512, I=256, b=16, g=32, counts=None, fmt="mxfp8"),
+    # The small-block variant (int4, b <= 16, g = 128): partial and full
+    # 16-row tiles, an empty expert and a count past the capacity.
+    dict(E=6, cap=37, H=1024, I=384, b=16, g=128, counts=[37, 0, 5, 16, 17, 40], fmt="int4"),
+    dict(E=4, cap=9, H=256, I=128, b=8, g=128, counts=[9, 3, 0, 12], fmt="int4"),
 ]
 
 

@@ -97,6 +97,12 @@ RAGGED = [
     dict(M=3, H=2080, I=128, E=8, k=2, b=8, g=32),
     dict(M=2, H=4096, I=256, E=8, k=4, b=8, g=32, fmt="mxfp8"),
     dict(M=3, H=2080, I=128, E=8, k=2, b=8, g=32, fmt="mxfp8"),
+    # The grouped small-block variant (int4, b <= 16, groups of 128 or
+    # more, K <= 2048): nine gate/up slabs (the weight-load window refills
+    # once), fifteen down slabs, and blocks filled to all 16 columns.
+    dict(M=11, H=1152, I=384, E=16, k=4, b=8, g=128),
+    dict(M=7, H=2048, I=1920, E=8, k=3, b=16, g=128),
+    dict(M=33, H=640, I=256, E=4, k=2, b=16, g=128),
     # An odd number of 128-element slabs in the down GEMM (three), on both
     # rings and both formats.
     dict(M=24, H=384, I=384, E=16, k=5, b=16, g=128),
