@@ -73,8 +73,9 @@ typedef enum {
                             chosen path's shape rules fail, the other path */
   MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
   MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised MFMA grouped GEMMs + combine; needs H and I
-                            multiples of 128, b <= 64 and (int4) K/group <= 32 with group
-                            dividing 128 or a multiple of it */
+                            multiples of 128, b <= 64, at most 128 scale groups per row
+                            (K/group; MXFP8: K/32) and (int4) group dividing 128 or a
+                            multiple of it */
 } moe_path;
 
 /* One projection's resident packed weights for all E experts. */
@@ -221,6 +222,22 @@ MOE_API moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t
                                    const int32_t* expert_block_ids,
                                    const int32_t* num_padded, size_t capacity, float* y,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_ffn_forward that also writes the W13 outputs of every valid route,
+ * the sums the gate/up kernels form before the activation: w13_out fp32
+ * [M*k][2I], columns 0..I-1 gate = W13g[e] x_t and I..2I-1 up = W13u[e] x_t
+ * (16-byte aligned, device, caller-owned; rows of invalid routes are left as
+ * they were). With the intermediate (moe_ffn_intermediate), the grouped
+ * path's routed-W2 rows (moe_ffn_route_outputs) and y, these are the four
+ * surfaces "Route-Block Membership Selects Packed-AWQ Arithmetic" captures
+ * (W13 output, activation, routed-W2 output, final output; the paragraph on
+ * the sparse native differences). The same kernels run, with one extra store
+ * per output; y and the other surfaces are bitwise those of moe_ffn_forward.
+ * Errors as moe_ffn_forward, and MOE_ERR_INVALID_ARG for a null or
+ * misaligned w13_out. */
+MOE_API moe_status moe_ffn_forward_capture(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                                           const float* topk_w, float* y, void* ws, size_t ws_bytes,
+                                           float* w13_out, hipStream_t stream);
 
 /* Same as moe_ffn_forward, and records the start and end of kernel i (in
  * launch order, the kernels moe_ffn_kernel_name lists) into events[2i] and

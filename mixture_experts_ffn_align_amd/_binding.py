@@ -66,6 +66,8 @@ _SIGNATURES = {
     "moe_ffn_forward_noalloc": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                          _c_ptr]),
     "moe_ffn_noalloc_max_bytes": (_c_size, []),
+    "moe_ffn_forward_capture": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                         _c_ptr, _c_size, _c_ptr, _c_ptr]),
     "moe_ffn_forward_profiled": (_c_i32, [ctypes.POINTER(moe_ffn_desc), _c_ptr, _c_ptr, _c_ptr,
                                           _c_ptr, _c_ptr, _c_size, _c_ptr,
                                           ctypes.POINTER(_c_ptr), _c_i32]),
@@ -301,6 +303,17 @@ def moe_ffn_forward_aligned(desc: moe_ffn_desc, x, topk_ids, topk_w, sorted_rout
     if check:
         _check(st, "moe_ffn_forward_aligned")
     return st
+
+
+def moe_ffn_forward_capture(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, w13_out, stream=None) -> None:
+    """moe_ffn_forward that also writes the W13 outputs (gate, up) of every valid
+    route into w13_out, fp32 [M*k, 2I]."""
+    import torch
+    _check_layer_io(desc, x, topk_ids, topk_w, y, ws)
+    _expect("w13_out", w13_out, torch.float32, (desc.M * desc.k, 2 * desc.I), x.device)
+    _check(lib().moe_ffn_forward_capture(ctypes.byref(desc), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(y),
+                                         _ptr(ws), ws.numel() * ws.element_size(), _ptr(w13_out),
+                                         _stream(stream)), "moe_ffn_forward_capture")
 
 
 def moe_ffn_forward_profiled(desc: moe_ffn_desc, x, topk_ids, topk_w, y, ws, events,

@@ -149,7 +149,7 @@ constexpr int kStageDown = 2;
 moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const uint16_t* x,
                        const int32_t* ids, const float* w, float* y, void* ws,
                        const int32_t* a_sorted, const int32_t* a_blocks, const int32_t* a_npad,
-                       size_t a_cap, hipStream_t s, hipEvent_t* ev) {
+                       size_t a_cap, hipStream_t s, hipEvent_t* ev, float* w13_out = nullptr) {
   // Profiled calls: kernel i records its start in ev[2i] and its end in
   // ev[2i + 1] (see moe::LaunchTiming); the timing is removed on every exit.
   int kidx = 0;
@@ -177,6 +177,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
     moe::DecodeArgs p{};
     p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
     p.a_hi = at<uint16_t>(ws, L.off_a); p.a_lo = at<uint16_t>(ws, L.off_aux); p.y = y;
+    p.w13_out = w13_out;
     p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k;
     p.ebase = d->expert_base;
     p.max_workgroups = d->max_workgroups;
@@ -195,6 +196,7 @@ moe_status run_forward(const moe_ffn_desc* d, const Layout& L, int stages, const
   p.x = x; p.ids = ids; p.topk_w = w; p.w13 = d->w13; p.w2 = d->w2;
   p.a16 = at<uint16_t>(ws, L.off_a); p.a_scale = at<float>(ws, L.off_aux);
   p.yhat = at<float>(ws, L.off_yhat); p.y = y;
+  p.w13_out = w13_out;
   p.M = d->M; p.H = d->H; p.I = d->I; p.E = d->E; p.k = d->k; p.b = d->b;
   p.ebase = d->expert_base;
   p.max_workgroups = d->max_workgroups;
@@ -365,6 +367,19 @@ moe_status moe_ffn_forward_aligned(const moe_ffn_desc* d, const uint16_t* x,
   if (capacity < capacity_of(d->M, d->k, d->E, d->b)) return MOE_ERR_CAPACITY;
   return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, sorted_route_ids,
                      expert_block_ids, num_padded, capacity, stream, nullptr);
+}
+
+moe_status moe_ffn_forward_capture(const moe_ffn_desc* d, const uint16_t* x, const int32_t* topk_ids,
+                                   const float* topk_w, float* y, void* ws, size_t ws_bytes, float* w13_out,
+                                   hipStream_t stream) {
+  Layout L;
+  moe_status st = validate(d, &L, false);
+  if (st != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  if ((st = check_io(d, x, topk_ids, topk_w, y, ws, ws_bytes, L)) != MOE_OK) return st;
+  if (w13_out == nullptr || !aligned(w13_out, 16)) return MOE_ERR_INVALID_ARG;
+  return run_forward(d, L, kStageGateUp | kStageDown, x, topk_ids, topk_w, y, ws, nullptr, nullptr, nullptr, 0,
+                     stream, nullptr, w13_out);
 }
 
 moe_status moe_ffn_forward_profiled(const moe_ffn_desc* d, const uint16_t* x,

@@ -108,12 +108,14 @@ __device__ __forceinline__ float dot_chunk(const ChunkRow<kFmt>& w, const uint32
   return d;
 }
 
-template <int kFmt>
+// kCapture: also write the W13 outputs (gate, up) to w13_out; a separate
+// instantiation, so the plain kernel carries no trace of it.
+template <int kFmt, bool kCapture>
 __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ sc,
     const uint8_t* __restrict__ zp, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
-    int mk, int k, int E, int ebase, int H, int I, int g_shift) {
+    float* __restrict__ w13_out, int mk, int k, int E, int ebase, int H, int I, int g_shift) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
   const int lane = threadIdx.x & (kWave - 1);
   // Task indices are wave-uniform: keep them (and the row addresses) scalar.
@@ -234,6 +236,11 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
       const size_t off = static_cast<size_t>(r) * I + i0 + lane;
       a_hi[off] = __builtin_bit_cast(uint16_t, h);
       a_lo[off] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v - static_cast<float>(h)));
+      if constexpr (kCapture) {
+        // The W13 outputs themselves (capture surface): gate, then up.
+        w13_out[static_cast<size_t>(r) * (2 * I) + i0 + lane] = gv;
+        w13_out[static_cast<size_t>(r) * (2 * I) + I + i0 + lane] = uv;
+      }
     }
   }
 }
@@ -482,18 +489,29 @@ bool decode_shape_ok(int fmt, int H, int I, int k, int g13, int g2) {
          (H % kDownRows) == 0 && k >= 1 && k <= 2 * kDownWaves;
 }
 
+namespace {
+
+template <int kFmt, bool kCapture>
+void launch_gate_up(const DecodeArgs& p, int wgs, hipStream_t stream) {
+  launch(decode_gate_up<kFmt, kCapture>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids,
+         static_cast<const unsigned char*>(p.w13.q), static_cast<const unsigned char*>(p.w13.scale), p.w13.zero,
+         p.a_hi, p.a_lo, p.w13_out, p.M * p.k, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
+}
+
+}  // namespace
+
 hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
   const int mk = p.M * p.k;
   const int64_t waves = int64_t(mk) * (p.I / kNpw);
   const int wgs = grid_for((waves + kGateUpWaves - 1) / kGateUpWaves, p.max_workgroups);
-  const auto* q = static_cast<const unsigned char*>(p.w13.q);
-  const auto* s = static_cast<const unsigned char*>(p.w13.scale);
-  if (p.w13.fmt == MOE_W_MXFP8)
-    launch(decode_gate_up<MOE_W_MXFP8>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q, s,
-                       p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
-  else
-    launch(decode_gate_up<MOE_W_INT4_AWQ>, dim3(wgs), dim3(kGateUpThreads), 0, stream, p.x, p.ids, q,
-                       s, p.w13.zero, p.a_hi, p.a_lo, mk, p.k, p.E, p.ebase, p.H, p.I, log2_of(p.w13.group));
+  const bool cap = p.w13_out != nullptr;
+  if (p.w13.fmt == MOE_W_MXFP8) {
+    if (cap) launch_gate_up<MOE_W_MXFP8, true>(p, wgs, stream);
+    else launch_gate_up<MOE_W_MXFP8, false>(p, wgs, stream);
+  } else {
+    if (cap) launch_gate_up<MOE_W_INT4_AWQ, true>(p, wgs, stream);
+    else launch_gate_up<MOE_W_INT4_AWQ, false>(p, wgs, stream);
+  }
   return hipGetLastError();
 }
 

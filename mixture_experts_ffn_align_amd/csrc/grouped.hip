@@ -62,7 +62,7 @@ constexpr int kThreads = 256;            // combine workgroup
 constexpr int kTileRows = 64;            // weight rows per row set of a GEMM tile (four waves of 16)
 constexpr int kMaxTok = 64;              // block size limit: four 16-column sub-tiles
 constexpr int kMaxSub = kMaxTok / 16;
-constexpr int kMaxGpr = 32;              // K / g limit (the tile's scales live in LDS)
+constexpr int kMaxGpr = 128;             // K / g limit (the tile's scales live in LDS)
 
 constexpr int kSteps = 4;                // 32-element MFMA steps per slab
 constexpr int kSlabK = 32 * kSteps;      // reduction elements per slab
@@ -210,6 +210,7 @@ struct GemmParams {
   uint16_t* a16;                 // gate/up output: fp16 [Mk][I], scaled per 64-neuron chunk
   float* a_scale;                // gate/up output: [Mk][I/128][4], entries 0, 1 undo the two chunks' scaling
   float* yhat;                   // down output [Mk][H]
+  float* w13_out;                // gate/up: fp32 [Mk][2I] W13 outputs (gate, up) or null
   int mk, k, E, b, nblk;
   int ntile;                     // tiles per block
   int rows_per_expert;           // weight rows per expert (2I or H)
@@ -217,6 +218,7 @@ struct GemmParams {
   int tile_stride;               // row offset between tiles (64 or 128)
   int out_rows;                  // row length of the output (I or H)
   int K, g;
+  int sc_set, zp_set;            // LDS bytes per row set of the tile's scales / zeros (set at launch)
 };
 
 constexpr int kGemmWaves = 8;
@@ -259,8 +261,6 @@ void grouped_gemm(const GemmParams p) {
   constexpr int kRowBytes = kMx ? kSlabK : kSlabK / 2; // weight bytes per row and slab
   constexpr int kRowsPerDma = 1024 / kRowBytes;        // weight rows per 1 KB LDS-DMA
   constexpr int kABytes = 2 * kTileRows * kRowBytes;   // weight bytes per slab (128 rows)
-  constexpr int kScStride = kTileRows * kMaxGpr * 2;   // bytes per row set (fp16 scales)
-  constexpr int kZpStride = kTileRows * kMaxGpr;       // bytes per row set (u8 zeros)
   constexpr int kADma = kABytes / 1024;                // weight DMAs per slab
   static_assert(kADma == 4 || kADma == 8 || kADma == 16, "weight DMAs per slab");
   // The pipeline keeps at least two slots in flight at the largest slot (every
@@ -268,8 +268,11 @@ void grouped_gemm(const GemmParams p) {
   static_assert(kRing >= 2 * Ring<kFmt, kGateUp, kSmall>::kSlotMax, "ring holds two slabs");
   static_assert(kABytes == Ring<kFmt, kGateUp, kSmall>::kABytes, "weight bytes per slab");
   __shared__ __align__(16) unsigned char ring[kRing];
-  __shared__ __align__(16) unsigned char ssh[2 * kScStride];
-  __shared__ __align__(16) unsigned char szz[kMx ? 16 : 2 * kZpStride];
+  // The tile's scales and zeros, two row sets each, sized per launch
+  // (p.sc_set, p.zp_set bytes per set: whole 1 KB DMA pieces).
+  extern __shared__ __align__(16) unsigned char dyn_lds[];
+  unsigned char* ssh = dyn_lds;
+  unsigned char* szz = dyn_lds + 2 * p.sc_set;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
@@ -364,14 +367,17 @@ void grouped_gemm(const GemmParams p) {
       const int nsc = (kTileRows * gpr * kScBytes) / 16, nzp = kMx ? 0 : (kTileRows * gpr) / 16;
       const unsigned char* gsc = p.sc + r0 * gpr * kScBytes;
       const unsigned char* gzp = kMx ? p.sc : p.zp + r0 * gpr;
+      // Waves 4 set .. 4 set + 3 move this set's pieces, every fourth each.
       const int w0 = set * 4;
-      for (int m = wave - w0; m >= 0 && m < 4 && m * kWave < nsc; m += 4) {
-        const int c = m * kWave + lane;
-        dma16(gsc + 16 * (c < nsc ? c : 0), lds_addr(ssh + set * kScStride + m * 1024));
-      }
-      for (int m = wave - w0; m >= 0 && m < 4 && m * kWave < nzp; m += 4) {
-        const int c = m * kWave + lane;
-        dma16(gzp + 16 * (c < nzp ? c : 0), lds_addr(szz + set * kZpStride + m * 1024));
+      if (wave >= w0 && wave < w0 + 4) {
+        for (int m = wave - w0; m * kWave < nsc; m += 4) {
+          const int c = m * kWave + lane;
+          dma16(gsc + 16 * (c < nsc ? c : 0), lds_addr(ssh + set * p.sc_set + m * 1024));
+        }
+        for (int m = wave - w0; m * kWave < nzp; m += 4) {
+          const int c = m * kWave + lane;
+          dma16(gzp + 16 * (c < nzp ? c : 0), lds_addr(szz + set * p.zp_set + m * 1024));
+        }
       }
     }
 
@@ -455,8 +461,8 @@ void grouped_gemm(const GemmParams p) {
     constexpr int kAStep = kMx ? 32 * kRowsPerDma : 16 * kRowsPerDma;   // LDS bytes per step
     // Scale and zero addresses of this lane (group 0); the group index is
     // added per partial.
-    const unsigned char* sp = ssh + rs * kScStride + (rl + 4 * lq) * gpr * kScBytes;
-    const unsigned char* zpl = szz + rs * kZpStride + (rl + n) * gpr;
+    const unsigned char* sp = ssh + rs * p.sc_set + (rl + 4 * lq) * gpr * kScBytes;
+    const unsigned char* zpl = szz + rs * p.zp_set + (rl + n) * gpr;
     // Group of the first partial of a slab: slab s covers groups s * gps ..
     // (g below the slab) or group s / spg (g a multiple of the slab).
     // B operand of step j for lane (n, lq): column n, piece 4 (j & 1) + lq
@@ -589,6 +595,15 @@ void grouped_gemm(const GemmParams p) {
         for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
           const floatx4 up = *reinterpret_cast<const floatx4*>(xch + ((wave * kSub + u) * kWave + lane) * 4);
+          if (p.w13_out != nullptr) {
+            // The W13 outputs themselves (capture surface): gate, then up.
+            const int r = __shfl(rc, 16 * act[u] + n, kWave);
+            if (r >= 0) {
+              float* o = p.w13_out + static_cast<size_t>(r) * (2 * p.out_rows) + ng * p.tile_stride + rl + 4 * lq;
+              *reinterpret_cast<float4*>(o) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+              *reinterpret_cast<float4*>(o + p.out_rows) = make_float4(up[0], up[1], up[2], up[3]);
+            }
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[u][i] = silu_mul(acc[u][i], up[i]);
           const float m = max_over_rows(
@@ -690,20 +705,27 @@ bool group_ok(int K, int g, int slab) {
 }
 
 template <int kFmt, bool kGateUp, bool kSmall>
-hipError_t launch_gemm_ring(const GemmParams& gp, int wgs, hipStream_t stream) {
+hipError_t launch_gemm_ring(const GemmParams& gp_in, int wgs, hipStream_t stream) {
+  // The tile's scales (and int4 zeros) for all K / g groups of its two row
+  // sets, each set rounded up to whole 1 KB DMA pieces.
+  GemmParams gp = gp_in;
+  const int gpr = gp.K / gp.g;
+  const int sc_bytes = kFmt == MOE_W_MXFP8 ? 1 : 2;
+  gp.sc_set = (kTileRows * gpr * sc_bytes + 1023) / 1024 * 1024;
+  gp.zp_set = kFmt == MOE_W_MXFP8 ? 0 : (kTileRows * gpr + 1023) / 1024 * 1024;
+  const uint32_t lds = static_cast<uint32_t>(2 * gp.sc_set + 2 * gp.zp_set);
   if constexpr (kFmt == MOE_W_MXFP8) {
-    launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+    launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
   } else {
     switch (flush_steps(gp.g, kSteps)) {
       case 1:
-        launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+        launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
         break;
       case 2:
-        launch(grouped_gemm<kFmt, kGateUp, 2, kSmall>, dim3(wgs), dim3(kGemmThreads), 0, stream, gp);
+        launch(grouped_gemm<kFmt, kGateUp, 2, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
         break;
       default:
-        launch(grouped_gemm<kFmt, kGateUp, kSteps, kSmall>, dim3(wgs), dim3(kGemmThreads), 0,
-                           stream, gp);
+        launch(grouped_gemm<kFmt, kGateUp, kSteps, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
         break;
     }
   }
@@ -729,10 +751,9 @@ hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t strea
 bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2) {
   // Whole slabs and whole tiles in both GEMMs (gate/up: 64 neurons; down:
   // 128 rows; 128-element slabs); the tile's scales (and int4 zeros) are
-  // staged in LDS: int4 at most 32 groups per row, MXFP8 at most 64 blocks
-  // of 32 per row.
+  // staged in LDS: at most 128 groups (int4) or blocks of 32 (MXFP8) per row.
   if (b < 1 || b > kMaxTok || (H % kSlabK) != 0 || (I % kSlabK) != 0) return false;
-  if (fmt == MOE_W_MXFP8) return g13 == 32 && g2 == 32 && H / 32 <= 2 * kMaxGpr && I / 32 <= 2 * kMaxGpr;
+  if (fmt == MOE_W_MXFP8) return g13 == 32 && g2 == 32 && H / 32 <= kMaxGpr && I / 32 <= kMaxGpr;
   return group_ok(H, g13, kSlabK) && group_ok(I, g2, kSlabK);
 }
 
@@ -747,6 +768,7 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.zp = p.w13.zero;
   gp.a16 = p.a16;
   gp.a_scale = p.a_scale;
+  gp.w13_out = p.w13_out;
   gp.mk = p.M * p.k;
   gp.k = p.k;
   gp.E = p.E;

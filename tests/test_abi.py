@@ -199,6 +199,11 @@ def test_forward_validation_enqueues_nothing():
               None) == B.MOE_ERR_INVALID_ARG
     assert fa(ctypes.byref(dg), FAKE, FAKE, FAKE, None, FAKE, FAKE, cap, FAKE, FAKE, need,
               None) == B.MOE_ERR_INVALID_ARG
+    # capture variant: the W13 output buffer is required and 16-byte aligned
+    cap_fn = L.moe_ffn_forward_capture
+    dd = ctypes.byref(_desc(M=1))
+    assert cap_fn(dd, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, None, None) == B.MOE_ERR_INVALID_ARG
+    assert cap_fn(dd, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, FAKE + 4, None) == B.MOE_ERR_INVALID_ARG
     # profiled variant: two events (start, end) per kernel
     ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
     assert L.moe_ffn_forward_profiled(ctypes.byref(_desc(M=1)), FAKE, FAKE, FAKE, FAKE, FAKE,

@@ -103,6 +103,12 @@ RAGGED = [
     dict(M=11, H=1152, I=384, E=16, k=4, b=8, g=128),
     dict(M=7, H=2048, I=1920, E=8, k=3, b=16, g=128),
     dict(M=33, H=640, I=256, E=4, k=2, b=16, g=128),
+    # Up to 128 scale groups per row on the grouped path (the tile's scales
+    # are staged in LDS sized per launch): int4 g = 32 at H = 2048 (64
+    # groups), H = 4096 (128 groups), and MXFP8 at H = 4096 (128 blocks).
+    dict(M=40, H=2048, I=256, E=8, k=2, b=16, g=32),
+    dict(M=48, H=4096, I=256, E=8, k=2, b=64, g=32),
+    dict(M=40, H=4096, I=256, E=8, k=2, b=16, g=32, fmt="mxfp8"),
     # An odd number of 128-element slabs in the down GEMM (three), on both
     # rings and both formats.
     dict(M=24, H=384, I=384, E=16, k=5, b=16, g=128),
@@ -231,3 +237,36 @@ def test_intermediate_beyond_fp16_range(factor, path):
     y = dw.forward(PATHS[path]).cpu().numpy()
     assert ffn_mismatch(y, ref["y"]) is None, ffn_errors(y, ref["y"])
     _check_intermediate(dw, ref, PATHS[path])
+
+
+# W13 outputs (gate and up before the activation): fp32 sums of exact
+# products over K = H elements. The bias-128 form sums x (128 + q) and then
+# removes (128 + z) sum x, so the fp32 rounding of sums about 20x larger than
+# the result (K up to 2048 terms, unit roundoff 2^-24) bounds the relative
+# error near 20 * sqrt(2048) * 2^-24 = 5e-5 in the worst case, far less in rms.
+W13_OUT_REL_L2 = 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "batch_m21", "batch_m256_zipf", "mxfp8_m64"])
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_w13_outputs_match_oracle(name, path):
+    # The fourth captured surface: gate and up per valid route, against the
+    # oracle's; and the capturing call leaves y bitwise as moe_ffn_forward's.
+    g = _gpu()
+    dw = g.device_workload(name)
+    st = g.oracle_stages(name)
+    cfg = dw.cfg
+    d = dw.layer.desc(cfg.M, PATHS[path])
+    ws = dw.layer.workspace(d)
+    out = torch.full((cfg.M * cfg.k, 2 * cfg.I), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.empty((cfg.M, cfg.H), dtype=torch.float32, device="cuda")
+    g.announce("w13-capture", name, path)
+    moe.moe_ffn_forward_capture(d, dw.x, dw.ids, dw.w, y, ws, out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    valid = (dw.wl.topk_ids.reshape(-1) >= 0) & (dw.wl.topk_ids.reshape(-1) < cfg.E)
+    for half, ref in ((got[:, :cfg.I], st["gate"]), (got[:, cfg.I:], st["up"])):
+        err = ffn_errors(half[valid], ref[valid])
+        assert err["rel_l2"] < W13_OUT_REL_L2, err
+    y0 = dw.forward(PATHS[path])
+    assert torch.equal(y0, y)
