@@ -41,6 +41,24 @@ def test_bench_reports_the_contract_fields():
     assert r["read_floor_us_same_bytes"] > 0
 
 
+def test_bench_runs_a_grouped_workload():
+    # Another workload through the same contract: the grouped path's GEMMs
+    # are timed by their own start/end events and the dominant one carries
+    # the roofline.
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "batch_m21", "--steps", "8",
+                          "--warmup", "2", "--replays", "3", "--no-extra", "--no-cpu-baseline"],
+                         cwd=ROOT, capture_output=True, text=True, timeout=150)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = [l for l in out.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, out.stdout[-2000:]
+    d = json.loads(lines[0])
+    assert d["config"]["path"] == "grouped" and d["config"]["M"] == 21 and d["value"] > 0
+    r = d["roofline"]
+    assert "grouped_gemm" in r["kernel"] and 0 < r["frac"] < 1 and r["read_floor_us_same_bytes"] > 0
+    assert set(r["kernel_us_all"]) == set(r["dispatch_event_us"])
+    assert d["cpu_baseline"] is None
+
+
 def test_measurement_kernels_read_and_copy_every_byte():
     # The streaming-read kernel's per-workgroup XORs combine to the XOR of
     # every word of the buffer, and the copy reproduces the buffer, on a size
