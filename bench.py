@@ -70,6 +70,31 @@ def source_hash(family):
     return h.hexdigest()[:16]
 
 
+def provenance(rot, seed=0):
+    """What reproduces the run: the seed, a SHA-256 of the generated inputs
+    (the packed weights of the first layer copy and every routing's x, IDs
+    and weights; the other layer copies are byte copies of it) and of the
+    library's sources and headers."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in (rot.w13_host, rot.w2_host):
+        for a in (p.q, p.s, p.z):
+            if a is not None:
+                h.update(np.ascontiguousarray(a).tobytes())
+    for x, ids, w in rot.host_inputs:
+        for a in (x, ids, w):
+            h.update(np.ascontiguousarray(a).tobytes())
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = hashlib.sha256()
+    for d in (os.path.join(root, "mixture_experts_ffn_align_amd", "csrc"), os.path.join(root, "include")):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".hpp", ".h")):
+                with open(os.path.join(d, f), "rb") as fh:
+                    src.update(f.encode() + b"\0" + fh.read())
+    return {"seed": seed, "inputs_sha256": h.hexdigest(), "sources_sha256": src.hexdigest(),
+            "layer_copies": len(rot.projections), "routings": len(rot.host_inputs)}
+
+
 def measured_traffic(kernel, workload, family):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     FETCH_SIZE / WRITE_SIZE counter passes (calibrated on a plain copy), or
@@ -934,6 +959,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_workloads": extra,
+        "provenance": provenance(rot),
     }
     if floor is not None:
         lf = floor[str(layer_bytes)]

@@ -11,7 +11,9 @@ import os
 import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_ffn.so")
+# The in-tree build; MOE_FFN_LIBRARY names another build of the same sources
+# (the host-sanitizer build of the tests, for one).
+LIB_PATH = os.environ.get("MOE_FFN_LIBRARY") or os.path.join(_PKG, "libmoe_ffn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_ffn.h")
 
 MOE_OK = 0

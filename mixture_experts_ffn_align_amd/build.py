@@ -36,9 +36,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(sources, out, verbose):
+def _compile(sources, out, verbose, extra=()):
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
+    cmd = [hipcc(), *FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}",
            *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -58,6 +58,38 @@ def build(verbose: bool = False) -> str:
     _compile(SOURCES, LIB, verbose)
     _compile(BENCH_SOURCES, BENCH_LIB, verbose)
     return LIB
+
+
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (each -fsanitize=
+# applies to the host pass only; the device code is built as usual).
+SANITIZE_HOST = [
+    "-O1", "-g",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """The layer library with instrumented host code, written to `out` (not
+    the in-tree library). Loading it needs the sanitizer runtime preloaded
+    (asan_runtime())."""
+    _compile(SOURCES, out, verbose, SANITIZE_HOST)
+    return out
+
+
+def asan_runtime() -> str | None:
+    """Path of the compiler's shared AddressSanitizer runtime, or None."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for cand in (clang, "/opt/rocm/llvm/bin/clang"):
+        if os.path.exists(cand):
+            res = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                                 capture_output=True, text=True)
+            path = res.stdout.strip()
+            if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    return None
 
 
 if __name__ == "__main__":

@@ -39,6 +39,8 @@ def test_bench_reports_the_contract_fields():
     assert d["copy_peak_GBps"] > 0 and 0 < d["hbm_frac_vs_floor"]
     assert d["warm_us_per_layer"] > 0
     assert r["read_floor_us_same_bytes"] > 0
+    pv = d["provenance"]
+    assert pv["seed"] == 0 and len(pv["inputs_sha256"]) == 64 and len(pv["sources_sha256"]) == 64
 
 
 def test_bench_runs_a_grouped_workload():
