@@ -117,6 +117,66 @@ RAGGED = [
 ]
 
 
+def _sampled_shapes(n, seed):
+    """Seeded random layer shapes inside what the library takes (decode: H and
+    I multiples of 32, power-of-two groups, k <= 16; grouped: H and I
+    multiples of 128, b <= 64, at most 128 groups per row), both weight
+    formats, block sizes that are not multiples of 16 among them, sized so
+    that the oracle takes about a second or less per shape."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        fmt = "mxfp8" if rng.random() < 0.25 else "int4"
+        H = int(128 * rng.integers(1, 33)) if rng.random() < 0.7 else int(32 * rng.integers(4, 129))
+        I = int(128 * rng.integers(1, 13)) if rng.random() < 0.7 else int(32 * rng.integers(1, 65))
+        if fmt == "mxfp8":
+            g = 32
+        else:
+            gs = [v for v in (32, 64, 128, 256) if H % v == 0 and I % v == 0]
+            if not gs:
+                continue
+            g = int(rng.choice(gs))
+        E = int(rng.integers(1, 257))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        b = int(rng.choice([1, 3, 8, 16, 24, 32, 48, 64]))
+        M = int(rng.integers(1, 81))
+        if E * H * I > (1 << (24 if fmt == "mxfp8" else 26)) or M * k * 3 * H * I > 1.5e9:
+            continue
+        shape = dict(M=M, H=H, I=I, E=E, k=k, b=b, g=g)
+        if fmt == "mxfp8":
+            shape["fmt"] = fmt
+        out.append(shape)
+    return out
+
+
+SAMPLED = _sampled_shapes(24, 2027)
+
+
+def _shape_id(s):
+    return "M{M}_H{H}_I{I}_E{E}_k{k}_b{b}_g{g}".format(**s) + ("_mx" if s.get("fmt") == "mxfp8" else "")
+
+
+@pytest.mark.parametrize("shape", SAMPLED, ids=_shape_id)
+def test_ffn_parity_sampled_shapes(shape):
+    # Both paths on one workload and one oracle run; a path that does not
+    # take the shape is left out (every shape fits at least one).
+    g = _gpu()
+    wl = _custom(13, **shape)
+    dw = g.DeviceWorkload(wl)
+    ref = oracle.ffn_stages(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
+    ran = 0
+    for name, path in PATHS.items():
+        st_code, _ = moe.moe_ffn_workspace_size(dw.layer.desc(wl.cfg.M, path), check=False)
+        if st_code == moe.MOE_ERR_UNSUPPORTED:
+            continue
+        g.announce("ffn-sampled", shape, name)
+        y = dw.forward(path).cpu().numpy()
+        assert ffn_mismatch(y, ref["y"]) is None, (name, ffn_errors(y, ref["y"]))
+        _check_intermediate(dw, ref, path)
+        ran += 1
+    assert ran >= 1
+
+
 @pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "M{M}_H{H}_I{I}_E{E}_k{k}_b{b}_g{g}".format(**s) + ("_mx" if s.get("fmt") == "mxfp8" else ""))
 @pytest.mark.parametrize("path", ["decode", "grouped"])
 def test_ffn_parity_ragged(shape, path):
