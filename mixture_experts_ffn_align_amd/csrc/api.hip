@@ -23,7 +23,7 @@ namespace {
 
 constexpr int32_t kMaxExperts = 2048;
 constexpr int64_t kMaxRoutes = int64_t(1) << 24;
-constexpr int32_t kAutoDecodeMaxM = 13;
+constexpr int32_t kAutoDecodeMaxM = 14;
 constexpr int64_t kMaxTasks = int64_t(1) << 30;
 
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -54,8 +54,8 @@ bool weights_ok(const moe_weights& w) {
 // MOE_PATH_AUTO: the decode path for M <= kAutoDecodeMaxM, else the grouped
 // path (expert-centric packing wins once tokens share experts: the warp-decode
 // write-up's last section). On the Qwen3-30B-A3B-sized layer (top-8 of 128
-// experts, int4 g128, b = 8, cold weights) the decode path is faster up to
-// M = 13, the two tie at M = 14 and the grouped path wins from M = 15
+// experts, int4 g128, b = 8, cold weights) the decode path is faster on the
+// median up to M = 14 and the grouped path from M = 15
 // (profiles/batch_sweep_decode_vs_grouped.md, `bench.py --batch-sweep`).
 int auto_path(const moe_ffn_desc* d) { return d->M <= kAutoDecodeMaxM ? MOE_PATH_DECODE : MOE_PATH_GROUPED; }
 

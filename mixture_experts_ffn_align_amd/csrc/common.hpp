@@ -127,4 +127,29 @@ __device__ __forceinline__ int load_expert(const int32_t* ids, int r, int E, int
   return (e >= 0 && e < E) ? e : -1;
 }
 
+// LDS byte address of a __shared__ object (low half of its generic address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// 16 bytes per lane from global memory to LDS at base + 16 * lane (LDS DMA).
+// M0 carries the LDS base; nothing else in these kernels uses M0.
+// It is issued from asm so that the compiler neither reorders it nor adds
+// waits for it: the kernel waits for these loads itself (s_waitcnt vmcnt;
+// the compiler's own waits stay right for loads issued after them).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 }  // namespace moe

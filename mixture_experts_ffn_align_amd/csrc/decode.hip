@@ -16,13 +16,14 @@
 //   fp32: s * (sum x(128+q) - (128+z) sum x). A DPP butterfly reduces each
 //   row; silu(gate) * up goes to the intermediate as a bf16 hi/lo pair
 //   (a = hi + lo to within 2^-17 relative).
-// Kernel 2 (down + combine): a workgroup owns kDownRows hidden outputs of
-//   one token; wave w takes the routes j = w, w+8, ... and folds the routing
-//   weight into its fp32 accumulators. Lanes of a wave form slots of
+// Kernel 2 (down + combine): a workgroup owns 8 (or, at larger M, 16)
+//   hidden outputs of one token; wave w takes the routes j = w, w+8, ... and
+//   folds the routing weight into its fp32 accumulators. Lanes of a wave form slots of
 //   pow2(I/32) lanes; a slot owns some of the rows and its lanes cover the
 //   I/32 chunks. Each lane loads its intermediate chunks (hi and lo planes)
-//   straight into registers, then its weight words, scales and zeros, so a
-//   route costs a single wait on memory; the weights are bf16 (128 + q)
+//   straight into registers (16-row form: the wave's LDS region, by LDS-DMA),
+//   then its weight words, scales and zeros, so a route costs a single wait
+//   on memory; the weights are bf16 (128 + q)
 //   pairs, each dotted with the hi and the lo plane. The eight wave partials
 //   are added in wave order and y is written once. No floating-point atomics
 //   anywhere.
@@ -104,6 +105,31 @@ __device__ __forceinline__ float dot_chunk(const ChunkRow<kFmt>& w, const uint32
 #pragma unroll
       for (int i = 0; i < 4; ++i) d = dot2_bf16(p[i], xw[4 * v + i], d);
     }
+  }
+  return d;
+}
+
+// Piece pc (16 bytes: activations 8 pc .. 8 pc + 7 of the chunk, as four
+// bf16 pairs xp) of dot_chunk, in dot_chunk's order: running pieces 0..3
+// through it gives dot_chunk's sum bit for bit.
+template <int kFmt>
+__device__ __forceinline__ float dot_piece(const ChunkRow<kFmt>& w, int pc, const uint32_t (&xp)[4],
+                                           uint32_t nib_mask, float d) {
+  if constexpr (kFmt == MOE_W_MXFP8) {
+    const uint4 v4 = w.v[pc >> 1];
+    const uint32_t w4[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t wd = w4[2 * (pc & 1) + h];
+      d = dot2_bf16(fp8x2_to_bf16x2<false>(wd), xp[2 * h], d);
+      d = dot2_bf16(fp8x2_to_bf16x2<true>(wd), xp[2 * h + 1], d);
+    }
+  } else {
+    const uint32_t w4[4] = {w.v[0].x, w.v[0].y, w.v[0].z, w.v[0].w};
+    uint32_t p[4];
+    unpack8_bias128_m(w4[pc], nib_mask, p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = dot2_bf16(p[i], xp[i], d);
   }
   return d;
 }
@@ -248,7 +274,11 @@ __global__ __launch_bounds__(kGateUpThreads) void decode_gate_up(
 // kSpan: lanes per slot, pow2(I/32) capped at 64; kCh: 32-element chunks of
 // a down row per lane (1, or 2 when I/32 > 64). Routes j = wave, wave + 8, ...
 // are taken in turn.
-template <int kFmt, int kCh, int kSpan>
+// kLds (one chunk per lane): the route's intermediate rows reach LDS by
+// LDS-DMA into a region of the wave's own and are read in 16-byte pieces
+// inside the dot products, so they hold no registers while in flight (more
+// workgroups per CU); same products, same order, same bits.
+template <int kFmt, int kCh, int kSpan, bool kLds, int kRows>
 __global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
@@ -257,11 +287,14 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     int g_shift) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
   constexpr int kSlots = kWave / kSpan;
-  constexpr int kRps = (kDownRows + kSlots - 1) / kSlots;  // rows per lane
-  __shared__ float part[kDownWaves][kDownRows];
+  constexpr int kRps = (kRows + kSlots - 1) / kSlots;  // rows per lane
+  static_assert(!kLds || kCh == 1, "LDS-staged intermediate: one chunk per lane");
+  constexpr int kPlane = kSpan * 64;                        // LDS bytes per intermediate plane
+  __shared__ float part[kDownWaves][kRows];
+  __shared__ __align__(16) unsigned char inter[kLds ? kDownWaves * 2 * kPlane : 16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
-  const int tiles_per_tok = H / kDownRows;
+  const int tiles_per_tok = H / kRows;
   const int ntiles = M * tiles_per_tok;
   const int nch = I >> 5, gpr = I >> g_shift;
   const int row_bytes = kMx ? I : I / 2;
@@ -279,18 +312,18 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
   for (int cc = 0; cc < kCh; ++cc) {
     const int c = c0 + cc * span;
     cl[cc] = c < nch ? c : 0;
-    cvalid[cc] = (c < nch && slot < kDownRows) ? 1.0f : 0.0f;
+    cvalid[cc] = (c < nch && slot < kRows) ? 1.0f : 0.0f;
   }
   int mrow[kRps];
 #pragma unroll
   for (int i = 0; i < kRps; ++i) {
     const int m = slot + i * slots;
-    mrow[i] = m < kDownRows ? m : 0;
+    mrow[i] = m < kRows ? m : 0;
   }
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t = tile / tiles_per_tok;
-    const int h0 = (tile - t * tiles_per_tok) * kDownRows;
+    const int h0 = (tile - t * tiles_per_tok) * kRows;
     float acc[kRps];
 #pragma unroll
     for (int i = 0; i < kRps; ++i) acc[i] = 0.0f;
@@ -300,12 +333,29 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
       // packed weights, then the scales and zeros.
       const size_t r = static_cast<size_t>(t) * k + j;
       uint4 hv[kCh][4], lv[kCh][4];
+      unsigned char* const ih = inter + (wave * 2) * kPlane;
+      if constexpr (kLds) {
+        // Both planes of the route's row, 1 KB per DMA (the plane's bytes in
+        // order; lanes past the row's 2I bytes re-read its start and land
+        // in the region's unused tail). The previous route's LDS reads have
+        // completed before its region is written again.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const unsigned char* hs = reinterpret_cast<const unsigned char*>(a_hi + r * I);
+        const unsigned char* ls = reinterpret_cast<const unsigned char*>(a_lo + r * I);
+        for (int m = 0; m * 1024 < 2 * I; ++m) {
+          const int off = 1024 * m + 16 * lane;
+          const int so = off < 2 * I ? off : 0;
+          dma16(hs + so, lds_addr(ih) + 1024 * m);
+          dma16(ls + so, lds_addr(ih + kPlane) + 1024 * m);
+        }
+      } else {
 #pragma unroll
-      for (int cc = 0; cc < kCh; ++cc) {
-        const uint4* hp = reinterpret_cast<const uint4*>(a_hi + r * I + (cl[cc] << 5));
-        const uint4* lp = reinterpret_cast<const uint4*>(a_lo + r * I + (cl[cc] << 5));
+        for (int cc = 0; cc < kCh; ++cc) {
+          const uint4* hp = reinterpret_cast<const uint4*>(a_hi + r * I + (cl[cc] << 5));
+          const uint4* lp = reinterpret_cast<const uint4*>(a_lo + r * I + (cl[cc] << 5));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) { hv[cc][v] = hp[v]; lv[cc][v] = lp[v]; }
+          for (int v = 0; v < 4; ++v) { hv[cc][v] = hp[v]; lv[cc][v] = lp[v]; }
+        }
       }
       // The scheduler must not move these loads below the expert-id wait,
       // nor (further down) the weight loads below the first use of any load.
@@ -339,6 +389,50 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kLds) {
+        // Every load of the route has landed (the DMAs are the oldest); the
+        // pieces are read in order, so each chain below sees the dwords in
+        // the register form's order.
+        wait_vm<0>();
+        const unsigned char* hc = ih + cl[0] * 64;
+        const unsigned char* lc = ih + kPlane + cl[0] * 64;
+        float sa4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float dh[kRps], dl[kRps];
+#pragma unroll
+        for (int i = 0; i < kRps; ++i) dh[i] = dl[i] = 0.0f;
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc) {
+          const uint4 h4 = *reinterpret_cast<const uint4*>(hc + 16 * pc);
+          const uint4 l4 = *reinterpret_cast<const uint4*>(lc + 16 * pc);
+          const uint32_t hp[4] = {h4.x, h4.y, h4.z, h4.w};
+          const uint32_t lp[4] = {l4.x, l4.y, l4.z, l4.w};
+          if constexpr (!kMx) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sa4[u] = dot2_bf16(lp[u], 0x3F803F80u, dot2_bf16(hp[u], 0x3F803F80u, sa4[u]));
+          }
+#pragma unroll
+          for (int i = 0; i < kRps; ++i) {
+            dh[i] = dot_piece<kFmt>(wv[0][i], pc, hp, nib_mask, dh[i]);
+            dl[i] = dot_piece<kFmt>(wv[0][i], pc, lp, nib_mask, dl[i]);
+            // One row's unpacked weights live at a time (registers, not ILP,
+            // bound this form: other waves fill the gaps).
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        const float sa = (sa4[0] + sa4[1]) + (sa4[2] + sa4[3]);
+#pragma unroll
+        for (int i = 0; i < kRps; ++i) {
+          if constexpr (kMx) {
+            const float s = cvalid[0] * e8m0_to_float(sv[0][i]);
+            acc[i] = fmaf(wr * s, dh[i] + dl[i], acc[i]);
+          } else {
+            const float s = cvalid[0] * half_bits_to_float(static_cast<uint16_t>(sv[0][i]));
+            const float zb = 128.0f + static_cast<float>(zv[0][i]);
+            acc[i] = fmaf(wr * s, fmaf(-zb, sa, dh[i] + dl[i]), acc[i]);
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int cc = 0; cc < kCh; ++cc) {
         const uint32_t hw[16] = {hv[cc][0].x, hv[cc][0].y, hv[cc][0].z, hv[cc][0].w,
@@ -378,24 +472,28 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     // Sum each row over the lanes of its slot: DPP butterflies inside 16-lane
     // rows, then (slots wider than 16 lanes) the row sums read out in lane
     // order. Fixed order, no LDS round trips.
-    if constexpr (kSpan == 32 && kRps == 4) {
-      // Two 32-lane slots, four rows each (slot s, index i: row s + 2i). A
-      // lane swap of 16-lane rows adds each slot's two halves and packs four
-      // rows into one register (16-lane rows: rows 0, 2, 1, 3 of a pair of
-      // indices), so two butterflies finish all eight rows.
-      const auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0]), __float_as_uint(acc[1]), false, false);
-      const auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[2]), __float_as_uint(acc[3]), false, false);
-      float v01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-      float v23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
-      v01 += dpp<0xB1>(v01);  v23 += dpp<0xB1>(v23);
-      v01 += dpp<0x4E>(v01);  v23 += dpp<0x4E>(v23);
-      v01 += dpp<0x141>(v01); v23 += dpp<0x141>(v23);
-      v01 += dpp<0x140>(v01); v23 += dpp<0x140>(v23);
-      if ((lane & 15) == 0) {
-        const int q = lane >> 4;
-        const int row = (q >> 1) | ((q & 1) << 1);
-        part[wave][row] = v01;
-        part[wave][row + 4] = v23;
+    if constexpr (kSpan == 32 && kRps % 4 == 0) {
+      // Two 32-lane slots (slot s, index i: row s + 2i), four indices at a
+      // time. A lane swap of 16-lane rows adds each slot's two halves and
+      // packs four rows into one register (16-lane rows: rows 0, 2, 1, 3 of
+      // a pair of indices), so two butterflies finish eight rows.
+#pragma unroll
+      for (int g4 = 0; g4 < kRps / 4; ++g4) {
+        const float* a = acc + 4 * g4;
+        const auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[1]), false, false);
+        const auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[2]), __float_as_uint(a[3]), false, false);
+        float v01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+        float v23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+        v01 += dpp<0xB1>(v01);  v23 += dpp<0xB1>(v23);
+        v01 += dpp<0x4E>(v01);  v23 += dpp<0x4E>(v23);
+        v01 += dpp<0x141>(v01); v23 += dpp<0x141>(v23);
+        v01 += dpp<0x140>(v01); v23 += dpp<0x140>(v23);
+        if ((lane & 15) == 0) {
+          const int q = lane >> 4;
+          const int row = 8 * g4 + ((q >> 1) | ((q & 1) << 1));
+          part[wave][row] = v01;
+          part[wave][row + 4] = v23;
+        }
       }
     } else if constexpr (kSpan == 64 && kRps == 8) {
       // One 64-lane slot, eight rows: each group of four accumulators folds
@@ -422,7 +520,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
       if (c0 == 0) {
 #pragma unroll
         for (int i = 0; i < kRps; ++i) {
-          if (slot + i * kSlots < kDownRows) part[wave][slot + i * kSlots] = acc[i];
+          if (slot + i * kSlots < kRows) part[wave][slot + i * kSlots] = acc[i];
         }
       }
     } else {
@@ -440,7 +538,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     }
     }
     __syncthreads();
-    if (threadIdx.x < kDownRows) {
+    if (threadIdx.x < kRows) {
       float v = part[0][threadIdx.x];
       for (int w = 1; w < kDownWaves; ++w) v += part[w][threadIdx.x];
       y[static_cast<size_t>(t) * H + h0 + threadIdx.x] = v;
@@ -455,26 +553,43 @@ int log2_of(int g) {
   return s;
 }
 
-template <int kFmt, int kCh, int kSpan>
-void launch_down(const DecodeArgs& p, int wgs, hipStream_t stream) {
-  launch(decode_down<kFmt, kCh, kSpan>, dim3(wgs), dim3(kDownThreads), 0, stream,
+template <int kFmt, int kCh, int kSpan, bool kLds, int kRows>
+void launch_down(const DecodeArgs& p, hipStream_t stream) {
+  const int wgs = grid_for(int64_t(p.M) * (p.H / kRows), p.max_workgroups);
+  launch(decode_down<kFmt, kCh, kSpan, kLds, kRows>, dim3(wgs), dim3(kDownThreads), 0, stream,
                      p.a_hi, p.a_lo, p.ids, p.topk_w, static_cast<const unsigned char*>(p.w2.q),
                      static_cast<const unsigned char*>(p.w2.scale), p.w2.zero, p.y, p.M, p.k, p.E,
                      p.ebase, p.H, p.I, log2_of(p.w2.group));
 }
 
+// Down workgroups of 16 rows with the intermediate staged in LDS (int4,
+// 17..32 chunks per row): each wave streams twice the weight bytes per route
+// at the same registers and workgroups per CU, once the layer has at least
+// two such workgroups per CU of the 256; below that the 8-row form keeps
+// more waves in flight.
+constexpr int kDownWideRows = 16;
+constexpr int64_t kDownWideMinGroups = 2 * 256;
+
 template <int kFmt>
-void launch_down_fmt(const DecodeArgs& p, int wgs, hipStream_t stream) {
+void launch_down_fmt(const DecodeArgs& p, hipStream_t stream) {
   const int nch = p.I >> 5;
+  const bool wide = (p.H % kDownWideRows) == 0 && int64_t(p.M) * (p.H / kDownWideRows) >= kDownWideMinGroups;
   if (nch > 32) {
-    if (nch > kWave) launch_down<kFmt, 2, 64>(p, wgs, stream);
-    else launch_down<kFmt, 1, 64>(p, wgs, stream);
-  } else if (nch > 16) launch_down<kFmt, 1, 32>(p, wgs, stream);
-  else if (nch > 8) launch_down<kFmt, 1, 16>(p, wgs, stream);
-  else if (nch > 4) launch_down<kFmt, 1, 8>(p, wgs, stream);
-  else if (nch > 2) launch_down<kFmt, 1, 4>(p, wgs, stream);
-  else if (nch > 1) launch_down<kFmt, 1, 2>(p, wgs, stream);
-  else launch_down<kFmt, 1, 1>(p, wgs, stream);
+    if (nch > kWave) launch_down<kFmt, 2, 64, false, kDownRows>(p, stream);
+    else launch_down<kFmt, 1, 64, false, kDownRows>(p, stream);
+  } else if (nch > 16) {
+    if constexpr (kFmt == MOE_W_INT4_AWQ) {
+      if (wide) {
+        launch_down<kFmt, 1, 32, true, kDownWideRows>(p, stream);
+        return;
+      }
+    }
+    launch_down<kFmt, 1, 32, false, kDownRows>(p, stream);
+  } else if (nch > 8) launch_down<kFmt, 1, 16, false, kDownRows>(p, stream);
+  else if (nch > 4) launch_down<kFmt, 1, 8, false, kDownRows>(p, stream);
+  else if (nch > 2) launch_down<kFmt, 1, 4, false, kDownRows>(p, stream);
+  else if (nch > 1) launch_down<kFmt, 1, 2, false, kDownRows>(p, stream);
+  else launch_down<kFmt, 1, 1, false, kDownRows>(p, stream);
 }
 
 }  // namespace
@@ -516,9 +631,8 @@ hipError_t launch_decode_gate_up(const DecodeArgs& p, hipStream_t stream) {
 }
 
 hipError_t launch_decode_down(const DecodeArgs& p, hipStream_t stream) {
-  const int wgs = grid_for(int64_t(p.M) * (p.H / kDownRows), p.max_workgroups);
-  if (p.w2.fmt == MOE_W_MXFP8) launch_down_fmt<MOE_W_MXFP8>(p, wgs, stream);
-  else launch_down_fmt<MOE_W_INT4_AWQ>(p, wgs, stream);
+  if (p.w2.fmt == MOE_W_MXFP8) launch_down_fmt<MOE_W_MXFP8>(p, stream);
+  else launch_down_fmt<MOE_W_INT4_AWQ>(p, stream);
   return hipGetLastError();
 }
 

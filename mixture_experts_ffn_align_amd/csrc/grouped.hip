@@ -150,30 +150,6 @@ __device__ __forceinline__ float max_over_rows(float v) {
   return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
-// LDS byte address of a __shared__ object (low half of its generic address).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// 16 bytes per lane from global memory to LDS at base + 16 * lane (LDS DMA).
-// M0 carries the LDS base; nothing else in these kernels uses M0.
-// It is issued from asm so that the compiler neither reorders it nor adds
-// waits for it; the kernel waits for these loads itself (wait_vm_le).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_base)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 // Wait until at most about n vector-memory operations of this wave are in
 // flight (n wave-uniform, rounded down to 0..4, 6, 8, 12, 16 or 24: a
 // smaller count only waits longer). Loads complete in issue order, so this
