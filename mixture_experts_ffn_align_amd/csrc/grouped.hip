@@ -368,13 +368,16 @@ void grouped_gemm(const GemmParams p) {
       const size_t grow = ebase + static_cast<size_t>(tr / kTileRows) * p.set_stride + tr % kTileRows;
       qa[t] = p.q + grow * row_bytes + 16 * ch;
     }
-    // This wave's activation DMAs (at most two per slab: nbdma <= 16):
+    // This wave's activation DMAs (at most kBMax per slab: nbdma <= 4 kSub):
     // DMA i = (u * kSteps + j) is issued by wave i % 8 and reads step j of
     // this lane's column in active sub-tile u.
-    const uint16_t* bsrc[2] = {p.b0, p.b0};
-    int boff[2] = {0, 0};
+    constexpr int kBMax = (kSub * kSteps + kGemmWaves - 1) / kGemmWaves;
+    const uint16_t* bsrc[kBMax];
+    int boff[kBMax];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kBMax; ++t) {
+      bsrc[t] = p.b0;
+      boff[t] = 0;
       const int i = wave + kGemmWaves * t;
       if (i >= nbdma) continue;
       const int j = i % kSteps;
@@ -403,23 +406,25 @@ void grouped_gemm(const GemmParams p) {
     // Ring slots are walked with running offsets, and the DMA sources with
     // running pointers: no divisions in the slab loop.
     const int ring_used = depth * slot_bytes;
-    const uint16_t* bnext0 = bsrc[0];
-    const uint16_t* bnext1 = bsrc[1];
+    const uint16_t* bnext[kBMax];
+#pragma unroll
+    for (int t = 0; t < kBMax; ++t) bnext[t] = bsrc[t];
     const unsigned char* anext[kAMax];
 #pragma unroll
     for (int t = 0; t < kAMax; ++t) anext[t] = qa[t];
     auto issue_next = [&](int off) {
       unsigned char* slot = ring + off;
-      if (my_b > 0) dma16(bnext0, lds_addr(slot + boff[0]));
-      if (my_b > 1) dma16(bnext1, lds_addr(slot + boff[1]));
+#pragma unroll
+      for (int t = 0; t < kBMax; ++t) {
+        if (t < my_b) dma16(bnext[t], lds_addr(slot + boff[t]));
+        bnext[t] += kSlabK;
+      }
 #pragma unroll
       for (int t = 0; t < kAMax; ++t) {
         if (t < my_a) dma16(anext[t], lds_addr(slot + (wave + kGemmWaves * t) * 1024));
         anext[t] += kRowBytes;
       }
       if (my_page) dma16(pnext, lds_addr(slot + page_off));
-      bnext0 += kSlabK;
-      bnext1 += kSlabK;
       pnext += 4;
     };
 
@@ -494,15 +499,22 @@ void grouped_gemm(const GemmParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) cs[i] = half_bits_to_float(sp16[i * gpr + grp]);
         }
-        uint4 A[kFlush];
-#pragma unroll
-        for (int jj = 0; jj < kFlush; ++jj) {
+        // Unpacked once per group for every active sub-tile; with one
+        // sub-tile (small blocks) each step's operand is formed right before
+        // its products instead, which keeps three of the four out of the
+        // registers.
+        auto a_operand = [&](int jj) {
           if constexpr (kMx) {
             const uint32_t* w = aw[kFlush * f + jj];
-            A[jj] = fp8_operand<kHalf>(w[0], w[1]);
+            return fp8_operand<kHalf>(w[0], w[1]);
           } else {
-            A[jj] = bias_pairs<kHalf>(aw[kFlush * f + jj][0], nib_mask);
+            return bias_pairs<kHalf>(aw[kFlush * f + jj][0], nib_mask);
           }
+        };
+        uint4 A[kSub > 1 ? kFlush : 1];
+        if constexpr (kSub > 1) {
+#pragma unroll
+          for (int jj = 0; jj < kFlush; ++jj) A[jj] = a_operand(jj);
         }
         // Down: the intermediate's scaling is uniform over 64-element chunks
         // (two steps), so a partial spans at most one chunk.
@@ -526,7 +538,8 @@ void grouped_gemm(const GemmParams p) {
               const int j = kFlush * f + jj;
               const uint4 B = *reinterpret_cast<const uint4*>(slot + kABytes + (u * kSteps + 2 * (j >> 1)) * 1024 +
                                                               ((j & 1) ? boff_b1 : boff_b0));
-              d = mfma16<kHalf>(A[jj], B, d);
+              const uint4 Aj = kSub > 1 ? A[kSub > 1 ? jj : 0] : a_operand(jj);
+              d = mfma16<kHalf>(Aj, B, d);
               if constexpr (!kMx) d = mfma16<kHalf>(Z, B, d);
             }
             if constexpr (kHalf) {
