@@ -109,6 +109,14 @@ RAGGED = [
     dict(M=40, H=2048, I=256, E=8, k=2, b=16, g=32),
     dict(M=48, H=4096, I=256, E=8, k=2, b=64, g=32),
     dict(M=40, H=4096, I=256, E=8, k=2, b=16, g=32, fmt="mxfp8"),
+    # The largest intermediate the decode path takes (I = 4096: two
+    # 32-element chunks per lane of a 64-lane slot in the down kernel) and a
+    # hidden size of 8192 (four chunks per lane in the decode gate/up
+    # kernel; 64 scale groups per row on the grouped path, MXFP8's 256
+    # blocks per row only on the decode path).
+    dict(M=2, H=512, I=4096, E=4, k=2, b=8, g=128),
+    dict(M=3, H=8192, I=256, E=4, k=2, b=16, g=128),
+    dict(M=2, H=8192, I=256, E=4, k=2, b=8, g=32, fmt="mxfp8"),
     # An odd number of 128-element slabs in the down GEMM (three), on both
     # rings and both formats.
     dict(M=24, H=384, I=384, E=16, k=5, b=16, g=128),
@@ -207,6 +215,23 @@ def test_ffn_invalid_ids_are_skipped(path):
     y = dw.forward(PATHS[path]).cpu().numpy()
     assert ffn_mismatch(y, ref) is None, ffn_errors(y, ref)
     assert np.all(y[5] == 0.0)
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_ffn_all_routes_invalid_gives_exact_zero(path):
+    # Every expert ID out of range (negative, E, far past E): every route is
+    # skipped, and every element of y, filled with NaN beforehand, is
+    # written as an exact zero.
+    g = _gpu()
+    wl = _custom(14, M=9, H=256, I=128, E=8, k=3, b=8, g=64)
+    bad = np.array([-1, 8, 1 << 20, -(1 << 30)], dtype=np.int32)
+    wl.topk_ids[:] = bad[np.arange(wl.topk_ids.size) % bad.size].reshape(wl.topk_ids.shape)
+    dw = g.DeviceWorkload(wl)
+    y = torch.full((wl.cfg.M, wl.cfg.H), float("nan"), device="cuda")
+    g.announce("ffn-all-invalid", path)
+    dw.layer.forward(dw.x, dw.ids, dw.w, y=y, path=PATHS[path])
+    torch.cuda.synchronize()
+    assert bool(torch.all(y == 0.0))
 
 
 @pytest.mark.parametrize("path", ["decode", "grouped"])
