@@ -490,6 +490,51 @@ def copy_peak(nbytes=1 << 30, replays=5):
             "checked": ok, "us_per_loads_per_lane": per}
 
 
+MFMA_ITERS = 2048      # per wave and chain: about 0.9 ms per launch at the data-sheet rate
+MFMA_GRID = 2048       # workgroups of four waves: eight per CU
+
+
+def mfma_peak(iters=MFMA_ITERS, grid=MFMA_GRID, replays=5):
+    """Dense MFMA rate of the measurement library's MFMA kernel (16x16x32,
+    bf16 and fp16 operands, fp32 accumulation, register operands, eight
+    independent chains per wave), each launch timed by its own start/end
+    events, median of replays. Each dtype is first run with every operand 1.0
+    and its per-wave sums checked exactly."""
+    import ctypes
+    import torch
+    import mixture_experts_ffn_align_amd as moe
+    L = moe._binding.bench_lib()
+    sink = torch.zeros(4 * grid, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)                          # creates the HIP events
+    z.record(stream)
+    torch.cuda.synchronize()
+    out = {"launch": f"{grid} workgroups x 4 waves x {iters} iterations x 8 independent chains of "
+                     f"16x16x32 MFMAs on register operands (seeded values in [1, 2))"}
+    for fp16, name in ((0, "bf16"), (1, "f16")):
+        check_iters = 64
+        sink.zero_()
+        if L.moe_bench_mfma(fp16, 0, check_iters, grid, sink.data_ptr(), None, None, None, stream.cuda_stream) != 0:
+            raise RuntimeError("moe_bench_mfma failed")
+        torch.cuda.synchronize()
+        ok = bool(torch.all(sink == 8 * 32 * check_iters).item())
+        flops = ctypes.c_double(0.0)
+        times = []
+        for _ in range(replays + 1):          # the first call is untimed
+            if L.moe_bench_mfma(fp16, 1, iters, grid, sink.data_ptr(), ctypes.byref(flops), a.cuda_event,
+                                z.cuda_event, stream.cuda_stream) != 0:
+                raise RuntimeError("moe_bench_mfma failed")
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(z) * 1e3)
+        us = statistics.median(times[1:])
+        tf = flops.value / (us * 1e-6) / 1e12
+        out[name] = {"TFLOPs": round(tf, 1), "us": round(us, 2), "frac_of_datasheet": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "checked": ok}
+    del sink
+    return out
+
+
 def copy_calibration():
     import torch
     n = 64 << 20
@@ -660,6 +705,8 @@ def grouped_sweep(fmt, gs=None, ns=None):
     per13 = full13.nbytes() / cfg.E
     per2 = full2.nbytes() / cfg.E
     rng = np.random.default_rng(0)
+    mp = mfma_peak()
+    log(json.dumps({"mfma_peak_measured": mp}))
     rows = []
     for G in (gs or SWEEP_G):
         def take(p):
@@ -698,12 +745,15 @@ def grouped_sweep(fmt, gs=None, ns=None):
                              "tflops_eff": round(flops / (us * 1e-6) / 1e12, 2),
                              "weight_GBps": round(G * per / (us * 1e-6) / 1e9, 1),
                              "hbm_frac": round(G * per / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+                             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                             "mfma_frac_vs_measured": round(flops / (us * 1e-6) / 1e12 /
+                                                            mp["bf16" if name == "gate_up" else "f16"]["TFLOPs"], 4)})
                 log(json.dumps(rows[-1]))
             del xb, a16, asc, yb
         del layers
         torch.cuda.empty_cache()
-    print(json.dumps({"grouped_sweep": fmt, "shapes": "Qwen3-30B-A3B H=2048 I=768", "rows": rows}), flush=True)
+    print(json.dumps({"grouped_sweep": fmt, "shapes": "Qwen3-30B-A3B H=2048 I=768", "mfma_peak_measured": mp,
+                      "rows": rows}), flush=True)
 
 
 def trace_phases(path, steps, warmup, replays):
@@ -886,10 +936,12 @@ def main():
 
     floor = None
     cp = None
+    mp = None
     if not args.no_floor:
-        log("streaming-read floor and copy peak")
+        log("streaming-read floor, copy peak and MFMA rate")
         floor = read_floor(sorted({int(alg[n]) for n in names if n in alg} | {int(touched * per_expert)}))
         cp = copy_peak()
+        mp = mfma_peak()
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -917,7 +969,10 @@ def main():
         for name in ("batch_m21", "batch_m256_zipf", "mxfp8_m64"):
             log("context workload", name)
             r2 = Rotation(CONFIGS[name], 8, 16)
-            extra[name] = rounded(layer_numbers(r2, 64, 3, args.replays, flush))
+            row = layer_numbers(r2, 64, 3, args.replays, flush)
+            if mp is not None:
+                row["mfma_frac_vs_measured_bf16"] = row["mfma_frac_bf16"] * BF16_PEAK_TFLOPS / mp["bf16"]["TFLOPs"]
+            extra[name] = rounded(row)
             del r2
             torch.cuda.empty_cache()
 
@@ -927,6 +982,8 @@ def main():
         cpu = cpu_baseline(rot, args.cpu_seconds)
 
     layer_bytes = int(touched * per_expert)
+    # Unpadded FLOPs of the routes (gate/up and down), per second.
+    layer_tflops = cfg.M * cfg.k * 2 * (3 * cfg.I * cfg.H) / (t_step * 1e-3) / 1e12
     fmt_name = f"int4 AWQ g{cfg.g}" if cfg.fmt == "int4" else "MXFP8 (E4M3, E8M0 per 32)"
     out = {
         "metric": "MoE-layer tokens/s and effective weight GB/s at M=1/21/256; % HBM/MFMA peak",
@@ -954,6 +1011,7 @@ def main():
         "ms_per_step_mean": round(st["mean"], 6),
         "effective_weight_GBps": round(layer_gbps, 1),
         "hbm_frac_layer": round(layer_gbps / HBM_PEAK_GBPS, 4),
+        "mfma_frac_layer_bf16": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
         "warm_us_per_layer": round(warm["median"] * 1e3, 3),
         "warm_note": "same layer copy and routing at every step: the touched experts stay cache-resident",
         "roofline": roofline,
@@ -966,6 +1024,8 @@ def main():
         out["read_floor"] = floor
         out["copy_peak_GBps"] = cp["GBps"]
         out["copy_peak"] = cp
+        out["mfma_peak_measured"] = mp
+        out["mfma_frac_layer_vs_measured_bf16"] = round(layer_tflops / mp["bf16"]["TFLOPs"], 4)
         out["hbm_frac_vs_floor"] = round(lf["graph_us_per_call"] / (t_step * 1e3), 4)
         out["hbm_frac_vs_floor_note"] = (f"one streaming-read kernel over the layer's {layer_bytes} weight bytes "
                                          f"takes {lf['graph_us_per_call']} us per call cold in a replayed graph "

@@ -1,10 +1,10 @@
 /*
  * moe_bench.h — measurement kernels for the MoE expert-FFN benchmark (not part
  * of the layer). They give the hardware floor the layer's kernels are set
- * against: the time a plain streaming read of the same bytes takes, and the
+ * against: the time a plain streaming read of the same bytes takes, the
  * copy-kernel bandwidth peak on the same GPU (the warp-decode write-up,
  * "Eficiencia de hardware", sets its bandwidth against a measured copy-kernel
- * peak).
+ * peak), and the dense MFMA rate the same GPU sustains.
  *
  * Conventions: device pointers owned by the caller; work is enqueued on
  * `stream`; nothing is allocated and the host is not synchronised.
@@ -48,6 +48,21 @@ MOE_BENCH_API int32_t moe_bench_stream_read(const void* src, size_t bytes, uint3
  * unsupported loads_per_lane), or 2. */
 MOE_BENCH_API int32_t moe_bench_copy(const void* src, void* dst, size_t bytes, int32_t loads_per_lane,
                                      hipEvent_t start, hipEvent_t stop, hipStream_t stream);
+
+/* Measures the dense MFMA rate: grid workgroups of four waves, each wave
+ * running 8 independent chains of `iters` 16x16x32 MFMAs (fp16 operands when
+ * fp16 != 0, else bf16; fp32 accumulation) on register operands, with no
+ * memory traffic. pattern 0 makes every operand 1.0 (each wave's lane 0 then
+ * writes exactly 8 * 32 * iters), pattern 1 seeded values in [1, 2).
+ *   sink        device, 4 * grid floats: one per wave
+ *   flops_out   host, optional: the FLOPs of the launch,
+ *               grid * 4 * iters * 8 * 16384
+ *   start/stop  optional events, as for moe_bench_stream_read
+ * The grouped GEMMs' MFMA fraction is set against this rate as well as
+ * against the data-sheet peak. Returns 0, 1 for bad arguments (null sink,
+ * iters or grid < 1, grid > 8192, pattern not 0 or 1), or 2. */
+MOE_BENCH_API int32_t moe_bench_mfma(int32_t fp16, int32_t pattern, int32_t iters, int32_t grid, float* sink,
+                                     double* flops_out, hipEvent_t start, hipEvent_t stop, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -99,6 +99,8 @@ _BENCH_SIGNATURES = {
     "moe_bench_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_ptr,
                                        _c_ptr, _c_ptr]),
     "moe_bench_copy": (_c_i32, [_c_ptr, _c_ptr, _c_size, _c_i32, _c_ptr, _c_ptr, _c_ptr]),
+    "moe_bench_mfma": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_ptr, ctypes.POINTER(ctypes.c_double), _c_ptr,
+                                _c_ptr, _c_ptr]),
 }
 
 

@@ -25,11 +25,16 @@ def test_library_exports_every_declared_symbol():
 
 def test_measurement_library_exports_and_validates():
     names = B.declared_symbols(B.BENCH_HEADER_PATH, "MOE_BENCH_API")
-    assert set(names) == {"moe_bench_stream_read", "moe_bench_copy"}
+    assert set(names) == {"moe_bench_stream_read", "moe_bench_copy", "moe_bench_mfma"}
     L = B.bench_lib()
     for n in names:
         assert hasattr(L, n)
-    rd, cp = L.moe_bench_stream_read, L.moe_bench_copy
+    rd, cp, mf = L.moe_bench_stream_read, L.moe_bench_copy, L.moe_bench_mfma
+    assert mf(0, 0, 64, 8, None, None, None, None, None) == 1
+    assert mf(0, 0, 0, 8, FAKE, None, None, None, None) == 1
+    assert mf(0, 0, 64, 0, FAKE, None, None, None, None) == 1
+    assert mf(0, 0, 64, 8193, FAKE, None, None, None, None) == 1
+    assert mf(1, 2, 64, 8, FAKE, None, None, None, None) == 1
     assert rd(None, 16, FAKE, 1, 4, None, None, None, None) == 1
     assert rd(FAKE, 17, FAKE, 1, 4, None, None, None, None) == 1
     assert rd(FAKE + 4, 16, FAKE, 1, 4, None, None, None, None) == 1

@@ -39,6 +39,10 @@ def test_bench_reports_the_contract_fields():
     assert d["copy_peak_GBps"] > 0 and 0 < d["hbm_frac_vs_floor"]
     assert d["warm_us_per_layer"] > 0
     assert r["read_floor_us_same_bytes"] > 0
+    mp = d["mfma_peak_measured"]
+    for dt in ("bf16", "f16"):
+        assert mp[dt]["checked"] is True and 0 < mp[dt]["TFLOPs"] < 1.2 * 2500
+    assert d["mfma_frac_layer_vs_measured_bf16"] > 0
     pv = d["provenance"]
     assert pv["seed"] == 0 and len(pv["inputs_sha256"]) == 64 and len(pv["sources_sha256"]) == 64
 
@@ -87,3 +91,27 @@ def test_measurement_kernels_read_and_copy_every_byte():
         got = np.bitwise_xor.reduce(sink[:grid.value].cpu().numpy().view(np.uint32))
         assert grid.value == -(-n // (256 * unroll * 16)) and got == want, unroll
         assert torch.equal(src, dst), unroll
+
+
+def test_measurement_mfma_kernel_runs_every_product():
+    # With every operand 1.0 each MFMA adds 32 to every accumulator element:
+    # each wave's lane 0 reports 8 chains x 32 x iters exactly, on every
+    # wave of the grid, for both operand types; the seeded pattern runs too.
+    import ctypes
+    import torch
+    from mixture_experts_ffn_align_amd import _binding as B
+    L = B.bench_lib()
+    s = torch.cuda.current_stream().cuda_stream
+    for fp16 in (0, 1):
+        for grid, iters in ((1, 1), (37, 5), (512, 64)):
+            sink = torch.full((4 * grid + 4,), -1.0, dtype=torch.float32, device="cuda")
+            flops = ctypes.c_double(0.0)
+            assert L.moe_bench_mfma(fp16, 0, iters, grid, sink.data_ptr(), ctypes.byref(flops), None, None, s) == 0
+            torch.cuda.synchronize()
+            assert torch.all(sink[:4 * grid] == 8 * 32 * iters), (fp16, grid, iters)
+            assert torch.all(sink[4 * grid:] == -1.0)
+            assert flops.value == grid * 4 * iters * 8 * 2 * 16 * 16 * 32
+        sink = torch.zeros(4 * 64, dtype=torch.float32, device="cuda")
+        assert L.moe_bench_mfma(fp16, 1, 16, 64, sink.data_ptr(), None, None, None, s) == 0
+        torch.cuda.synchronize()
+        assert torch.all(torch.isfinite(sink)) and torch.all(sink > 8 * 32 * 16)
