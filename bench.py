@@ -972,6 +972,8 @@ def main():
             row = layer_numbers(r2, 64, 3, args.replays, flush)
             if mp is not None:
                 row["mfma_frac_vs_measured_bf16"] = row["mfma_frac_bf16"] * BF16_PEAK_TFLOPS / mp["bf16"]["TFLOPs"]
+            if cp is not None:
+                row["hbm_frac_vs_copy_peak"] = row["effective_weight_GBps"] / cp["GBps"]
             extra[name] = rounded(row)
             del r2
             torch.cuda.empty_cache()
@@ -1024,6 +1026,7 @@ def main():
         out["read_floor"] = floor
         out["copy_peak_GBps"] = cp["GBps"]
         out["copy_peak"] = cp
+        out["hbm_frac_vs_copy_peak"] = round(layer_gbps / cp["GBps"], 4)
         out["mfma_peak_measured"] = mp
         out["mfma_frac_layer_vs_measured_bf16"] = round(layer_tflops / mp["bf16"]["TFLOPs"], 4)
         out["hbm_frac_vs_floor"] = round(lf["graph_us_per_call"] / (t_step * 1e3), 4)

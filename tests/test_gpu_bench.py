@@ -43,6 +43,7 @@ def test_bench_reports_the_contract_fields():
     for dt in ("bf16", "f16"):
         assert mp[dt]["checked"] is True and 0 < mp[dt]["TFLOPs"] < 1.2 * 2500
     assert d["mfma_frac_layer_vs_measured_bf16"] > 0
+    assert 0 < d["hbm_frac_vs_copy_peak"] < 1.5
     pv = d["provenance"]
     assert pv["seed"] == 0 and len(pv["inputs_sha256"]) == 64 and len(pv["sources_sha256"]) == 64
 
