@@ -73,8 +73,8 @@ typedef enum {
                             chosen path's shape rules fail, the other path */
   MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
   MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised MFMA grouped GEMMs + combine; needs H and I
-                            multiples of 128, b <= 64, at most 128 scale groups per row
-                            (K/group; MXFP8: K/32) and (int4) group dividing 128 or a
+                            multiples of 32 (as every path), b <= 64, at most 128 scale groups
+                            per row (K/group; MXFP8: K/32) and (int4) group dividing 128 or a
                             multiple of it */
 } moe_path;
 
@@ -277,7 +277,7 @@ MOE_API moe_status moe_ffn_down_combine(const moe_ffn_desc* d, const int32_t* to
  * [0, capacity]; rows past it are neither read nor written.
  *   xb        bf16 [E][capacity][H]            (gate/up input)
  *   a16       fp16 [E][capacity][I] and
- *   a_scale   fp32 [E][capacity][I/128][4]: silu(gate)*up in format 2 of
+ *   a_scale   fp32 [E][capacity][ceil(I/128)][4]: silu(gate)*up in format 2 of
  *             moe_ffn_intermediate (gate/up output, down input)
  *   yb        fp32 [E][capacity][H]            (down output, before any combine)
  *   counts    int32 [E] device
@@ -307,7 +307,7 @@ MOE_API const char* moe_ffn_kernel_name(const moe_ffn_desc* d, int32_t i);
  *   1 (decode path): a bf16 hi plane [M*k][I] at *offset and a bf16 lo plane
  *     at *aux_offset; a = hi + lo within 2^-17 relative.
  *   2 (grouped path): an fp16 plane [M*k][I] at *offset and fp32 multipliers
- *     [M*k][I/128][4] at *aux_offset; element i of route r is
+ *     [M*k][ceil(I/128)][4] at *aux_offset; element i of route r is
  *     fp16[r][i] * mult[r][i/128][(i/64) % 2] (entries 2 and 3 unused). Each
  *     64-element chunk is scaled by a power of two that puts its largest
  *     magnitude in [2^14, 2^15) before rounding to fp16, so every element is

@@ -350,25 +350,25 @@ def moe_ffn_down_combine(desc: moe_ffn_desc, topk_ids, topk_w, y, ws, stream=Non
 
 def moe_ffn_gate_up_batched(desc: moe_ffn_desc, xb, counts, a16, a_scale, stream=None) -> None:
     """xb [E, capacity, H] bf16, counts [E] int32 (device), a16 [E, capacity, I]
-    fp16 and a_scale [E, capacity, I/128, 4] fp32 (intermediate format 2)."""
+    fp16 and a_scale [E, capacity, ceil(I/128), 4] fp32 (intermediate format 2)."""
     import torch
     E, cap = desc.E, xb.shape[1] if xb.dim() == 3 else -1
     dev = _expect("xb", xb, torch.bfloat16, (E, cap, desc.H))
     _expect("counts", counts, torch.int32, (E,), dev)
     _expect("a16", a16, torch.float16, (E, cap, desc.I), dev)
-    _expect("a_scale", a_scale, torch.float32, (E, cap, desc.I // 128, 4), dev)
+    _expect("a_scale", a_scale, torch.float32, (E, cap, -(-desc.I // 128), 4), dev)
     _check(lib().moe_ffn_gate_up_batched(ctypes.byref(desc), _ptr(xb), _ptr(counts), xb.shape[1],
                                          _ptr(a16), _ptr(a_scale), _stream(stream)),
            "moe_ffn_gate_up_batched")
 
 
 def moe_ffn_down_batched(desc: moe_ffn_desc, a16, a_scale, counts, yb, stream=None) -> None:
-    """a16 [E, capacity, I] fp16 and a_scale [E, capacity, I/128, 4] fp32, counts [E]
+    """a16 [E, capacity, I] fp16 and a_scale [E, capacity, ceil(I/128), 4] fp32, counts [E]
     int32, yb [E, capacity, H] fp32."""
     import torch
     E, cap = desc.E, a16.shape[1] if a16.dim() == 3 else -1
     dev = _expect("a16", a16, torch.float16, (E, cap, desc.I))
-    _expect("a_scale", a_scale, torch.float32, (E, cap, desc.I // 128, 4), dev)
+    _expect("a_scale", a_scale, torch.float32, (E, cap, -(-desc.I // 128), 4), dev)
     _expect("counts", counts, torch.int32, (E,), dev)
     _expect("yb", yb, torch.float32, (E, cap, desc.H), dev)
     _check(lib().moe_ffn_down_batched(ctypes.byref(desc), _ptr(a16), _ptr(a_scale), _ptr(counts),

@@ -73,7 +73,7 @@ bool tasks_fit(int path, const moe_ffn_desc* d, int64_t mk) {
   if (path == MOE_PATH_DECODE) return mk * (I / 2) <= kMaxTasks && M * (H / 8) <= kMaxTasks;
   const int64_t nblk = static_cast<int64_t>(capacity_of(d->M, d->k, d->E, d->b)) / d->b;
   if (M * (H / 4) > kMaxTasks) return false;
-  return nblk * (I / 64) <= kMaxTasks && nblk * (H / 128) <= kMaxTasks;
+  return nblk * ((I + 63) / 64) <= kMaxTasks && nblk * ((H + 127) / 128) <= kMaxTasks;
 }
 
 moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
@@ -118,7 +118,7 @@ moe_status validate(const moe_ffn_desc* d, Layout* L, bool need_align_buffers) {
   L->align_ws = moe::align_ws_bytes(static_cast<int>(mk), d->E);
   L->off_align_ws = o; o += L->align_ws;
   L->off_a = o;      o += round256(size_t(mk) * d->I * sizeof(uint16_t));
-  L->off_aux = o;    o += round256(size_t(mk) * (d->I / 128) * 4 * sizeof(float));
+  L->off_aux = o;    o += round256(size_t(mk) * ((d->I + 127) / 128) * 4 * sizeof(float));
   L->off_yhat = o;   o += round256(size_t(mk) * d->H * sizeof(float));
   L->total = o;
   return MOE_OK;
@@ -445,7 +445,7 @@ moe_status validate_batched(const moe_ffn_desc* d, int32_t capacity) {
   if (int64_t(d->E) * capacity > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   // GEMM tasks: E * ceil(capacity / b) blocks times the tiles per block.
   const int64_t nblk = int64_t(d->E) * ((int64_t(capacity) + d->b - 1) / d->b);
-  if (nblk * (d->I / 64) > kMaxTasks || nblk * (d->H / 128) > kMaxTasks) return MOE_ERR_UNSUPPORTED;
+  if (nblk * ((d->I + 63) / 64) > kMaxTasks || nblk * ((d->H + 127) / 128) > kMaxTasks) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

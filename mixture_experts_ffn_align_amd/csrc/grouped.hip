@@ -184,7 +184,7 @@ struct GemmParams {
   const unsigned char* sc;       // int4: fp16 [E][rows][K/g]; MXFP8: E8M0 [E][rows][K/32]
   const uint8_t* zp;
   uint16_t* a16;                 // gate/up output: fp16 [Mk][I], scaled per 64-neuron chunk
-  float* a_scale;                // gate/up output: [Mk][I/128][4], entries 0, 1 undo the two chunks' scaling
+  float* a_scale;                // gate/up output: [Mk][ceil(I/128)][4], entries 0, 1 undo the two chunks' scaling
   float* yhat;                   // down output [Mk][H]
   float* w13_out;                // gate/up: fp32 [Mk][2I] W13 outputs (gate, up) or null
   int mk, k, E, b, nblk;
@@ -192,8 +192,9 @@ struct GemmParams {
   int rows_per_expert;           // weight rows per expert (2I or H)
   int set_stride;                // row offset of row set 1 (I: up rows; 64: next 64 rows)
   int tile_stride;               // row offset between tiles (64 or 128)
-  int out_rows;                  // row length of the output (I or H)
-  int K, g;
+  int out_rows;                  // row length of the output (I or H): output rows past it in the last
+                                 // tile are not written, and their weight rows are read as row out_rows - 1
+  int K, g;                      // K a multiple of 32: the last slab may hold fewer than four steps
   int sc_set, zp_set;            // LDS bytes per row set of the tile's scales / zeros (set at launch)
 };
 
@@ -227,7 +228,7 @@ struct Ring {
 // kSteps). kSmall: blocks of one sub-tile (b <= 16, which the launch
 // guarantees), a small ring and an 80-VGPR budget so that three workgroups
 // share a CU.
-template <int kFmt, bool kGateUp, int kFlush, bool kSmall>
+template <int kFmt, bool kGateUp, int kFlush, bool kSmall, bool kRagged>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(kSmall ? 6 : 1)))
 void grouped_gemm(const GemmParams p) {
   constexpr bool kMx = kFmt == MOE_W_MXFP8;
@@ -260,7 +261,11 @@ void grouped_gemm(const GemmParams p) {
   const int npad = batched ? 0 : p.num_padded[0];
   const int row_bytes = kMx ? p.K : p.K / 2, gpr = p.K / p.g;
   constexpr int kScBytes = kMx ? 1 : 2;                 // E8M0 byte or fp16 scale
-  const int nslab = p.K / kSlabK;
+  // kRagged: K or the output rows off the 128 grid (multiples of 32): the
+  // last slab may hold fewer than four MFMA steps and the last tile may
+  // reach past the output rows.
+  const int nslab = kRagged ? (p.K + kSlabK - 1) / kSlabK : p.K / kSlabK;
+  const int last_steps = kRagged ? (p.K - (nslab - 1) * kSlabK) / 32 : kSteps;
   const uint32_t nib_mask = in_vgpr(kNibMask<kHalf>);
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
@@ -334,39 +339,55 @@ void grouped_gemm(const GemmParams p) {
     wait_vm<0>();
 
     const size_t ebase = static_cast<size_t>(e) * p.rows_per_expert + static_cast<size_t>(ng) * p.tile_stride;
+    // First output row of row set `set` of this tile (gate/up: both sets
+    // cover the same 64 neurons), and how many of its 64 rows exist (at
+    // least 32 in set 0: out_rows is a multiple of 32).
+    auto set_first = [&](int set) { return ng * p.tile_stride + (kGateUp ? 0 : set * kTileRows); };
+    auto set_rows = [&](int set) { return kRagged ? min(max(p.out_rows - set_first(set), 0), kTileRows) : kTileRows; };
     // Scales and zeros of the tile's two row sets, all groups (whole 1 KB
-    // DMAs: lanes past a region re-read its first chunk and land in the
-    // set's unused tail).
+    // DMAs: lanes past a set's rows re-read the first chunk of set 0 and
+    // land in the set's unused tail).
 #pragma unroll
     for (int set = 0; set < 2; ++set) {
       const size_t r0 = ebase + static_cast<size_t>(set) * p.set_stride;
       const int nsc = (kTileRows * gpr * kScBytes) / 16, nzp = kMx ? 0 : (kTileRows * gpr) / 16;
+      const int vsc = (set_rows(set) * gpr * kScBytes) / 16, vzp = kMx ? 0 : (set_rows(set) * gpr) / 16;
       const unsigned char* gsc = p.sc + r0 * gpr * kScBytes;
       const unsigned char* gzp = kMx ? p.sc : p.zp + r0 * gpr;
+      const unsigned char* gsc0 = p.sc + ebase * gpr * kScBytes;
+      const unsigned char* gzp0 = kMx ? p.sc : p.zp + ebase * gpr;
       // Waves 4 set .. 4 set + 3 move this set's pieces, every fourth each.
       const int w0 = set * 4;
       if (wave >= w0 && wave < w0 + 4) {
         for (int m = wave - w0; m * kWave < nsc; m += 4) {
           const int c = m * kWave + lane;
-          dma16(gsc + 16 * (c < nsc ? c : 0), lds_addr(ssh + set * p.sc_set + m * 1024));
+          dma16(c < vsc ? gsc + 16 * c : gsc0, lds_addr(ssh + set * p.sc_set + m * 1024));
         }
         for (int m = wave - w0; m * kWave < nzp; m += 4) {
           const int c = m * kWave + lane;
-          dma16(gzp + 16 * (c < nzp ? c : 0), lds_addr(szz + set * p.zp_set + m * 1024));
+          dma16(c < vzp ? gzp + 16 * c : gzp0, lds_addr(szz + set * p.zp_set + m * 1024));
         }
       }
     }
 
     // Weight DMAs of this wave: DMA m covers tile rows kRowsPerDma * m ..
     // +kRowsPerDma-1; lane l takes row l % kRowsPerDma, chunk l / kRowsPerDma.
+    // Rows past out_rows read row out_rows - 1 of the same set; chunks of the
+    // last slab past its steps read the slab's first chunk (a_back bytes
+    // back) and are not used.
     const unsigned char* qa[kAMax];
+    int a_back[kAMax];
 #pragma unroll
     for (int t = 0; t < kAMax; ++t) {
       const int m = wave + kGemmWaves * t;
       const int tr = kRowsPerDma * (m < kADma ? m : 0) + lane % kRowsPerDma;     // tile-local row
       const int ch = lane / kRowsPerDma;
-      const size_t grow = ebase + static_cast<size_t>(tr / kTileRows) * p.set_stride + tr % kTileRows;
+      const int set = tr / kTileRows;
+      const int o = kRagged ? min(set_first(set) + tr % kTileRows, p.out_rows - 1) : set_first(set) + tr % kTileRows;
+      const size_t grow = static_cast<size_t>(e) * p.rows_per_expert +
+                          (kGateUp ? static_cast<size_t>(set) * p.set_stride : 0) + o;
       qa[t] = p.q + grow * row_bytes + 16 * ch;
+      a_back[t] = (kMx ? ch / 2 : ch) < last_steps ? 0 : 16 * ch;
     }
     // This wave's activation DMAs (at most kBMax per slab: nbdma <= 4 kSub):
     // DMA i = (u * kSteps + j) is issued by wave i % 8 and reads step j of
@@ -374,10 +395,12 @@ void grouped_gemm(const GemmParams p) {
     constexpr int kBMax = (kSub * kSteps + kGemmWaves - 1) / kGemmWaves;
     const uint16_t* bsrc[kBMax];
     int boff[kBMax];
+    int b_back[kBMax];                    // last slab: elements back to its first piece
 #pragma unroll
     for (int t = 0; t < kBMax; ++t) {
       bsrc[t] = p.b0;
       boff[t] = 0;
+      b_back[t] = 0;
       const int i = wave + kGemmWaves * t;
       if (i >= nbdma) continue;
       const int j = i % kSteps;
@@ -391,6 +414,9 @@ void grouped_gemm(const GemmParams p) {
       const int pc = (lane & 7) ^ (c >> 1);
       bsrc[t] = p.b0 + static_cast<size_t>(__shfl(bc, 16 * st + c, kWave)) * p.K + 64 * (j >> 1) + 8 * pc;
       boff[t] = kABytes + i * 1024;
+      // Pieces of the last slab past its steps read the slab's first piece.
+      const int eo = 64 * (j >> 1) + 8 * pc;
+      b_back[t] = eo < 32 * last_steps ? 0 : eo;
     }
     // Multiplier page (down): lane 16 u + c reads the 16-byte entry of column
     // c of active sub-tile u for the slab (lanes past the active sub-tiles
@@ -401,7 +427,7 @@ void grouped_gemm(const GemmParams p) {
       for (int v = lane >> 4; v > 0 && m != 0; --v) m &= m - 1;
       const int row_src = __shfl(bc, m != 0 ? 16 * __builtin_ctz(m) + n : n, kWave);
       const int row = m != 0 ? row_src : 0;
-      pnext = p.bsc + static_cast<size_t>(row) * (p.K / kSlabK) * 4;
+      pnext = p.bsc + static_cast<size_t>(row) * nslab * 4;
     }
     // Ring slots are walked with running offsets, and the DMA sources with
     // running pointers: no divisions in the slab loop.
@@ -412,16 +438,18 @@ void grouped_gemm(const GemmParams p) {
     const unsigned char* anext[kAMax];
 #pragma unroll
     for (int t = 0; t < kAMax; ++t) anext[t] = qa[t];
+    int issued = 0;                       // slabs issued so far
     auto issue_next = [&](int off) {
       unsigned char* slot = ring + off;
+      const bool tail = kRagged && ++issued == nslab;
 #pragma unroll
       for (int t = 0; t < kBMax; ++t) {
-        if (t < my_b) dma16(bnext[t], lds_addr(slot + boff[t]));
+        if (t < my_b) dma16(bnext[t] - (tail ? b_back[t] : 0), lds_addr(slot + boff[t]));
         bnext[t] += kSlabK;
       }
 #pragma unroll
       for (int t = 0; t < kAMax; ++t) {
-        if (t < my_a) dma16(anext[t], lds_addr(slot + (wave + kGemmWaves * t) * 1024));
+        if (t < my_a) dma16(anext[t] - (tail ? a_back[t] : 0), lds_addr(slot + (wave + kGemmWaves * t) * 1024));
         anext[t] += kRowBytes;
       }
       if (my_page) dma16(pnext, lds_addr(slot + page_off));
@@ -485,8 +513,11 @@ void grouped_gemm(const GemmParams p) {
           aw[j][0] = *reinterpret_cast<const uint32_t*>(slot + a_off + kAStep * j);
         }
       }
+      // The last slab may hold fewer steps (a multiple of kFlush: g divides K).
+      const int steps_here = kRagged && s == nslab - 1 ? last_steps : kSteps;
 #pragma unroll
       for (int f = 0; f < kSteps / kFlush; ++f) {
+        if (kFlush * f >= steps_here) break;
         const int grp = grp0 + f;
         uint4 Z;
         float cs[4];
@@ -579,6 +610,10 @@ void grouped_gemm(const GemmParams p) {
       // Gate waves: a = silu(gate) * up in place, and each column's largest
       // |a| over this wave's 16 neurons into LDS beside the hand-off area.
       float* xmax = xch + 4 * kSub * kWave * 4;    // [gate wave][active index][column]
+      // This lane's four neurons exist (out_rows is a multiple of 32, so the
+      // four are all in or all out); those that do not are left out of the
+      // chunk's maximum and not written.
+      const bool nvalid = !kRagged || ng * p.tile_stride + rl + 4 * lq < p.out_rows;
       if (rs == 0) {
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
@@ -587,14 +622,14 @@ void grouped_gemm(const GemmParams p) {
           if (p.w13_out != nullptr) {
             // The W13 outputs themselves (capture surface): gate, then up.
             const int r = __shfl(rc, 16 * act[u] + n, kWave);
-            if (r >= 0) {
+            if (r >= 0 && nvalid) {
               float* o = p.w13_out + static_cast<size_t>(r) * (2 * p.out_rows) + ng * p.tile_stride + rl + 4 * lq;
               *reinterpret_cast<float4*>(o) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
               *reinterpret_cast<float4*>(o + p.out_rows) = make_float4(up[0], up[1], up[2], up[3]);
             }
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[u][i] = silu_mul(acc[u][i], up[i]);
+          for (int i = 0; i < 4; ++i) acc[u][i] = nvalid ? silu_mul(acc[u][i], up[i]) : 0.0f;
           const float m = max_over_rows(
               fmaxf(fmaxf(fabsf(acc[u][0]), fabsf(acc[u][1])), fmaxf(fabsf(acc[u][2]), fabsf(acc[u][3]))));
           if (lq == 0) xmax[(wave * kSub + u) * 16 + n] = m;
@@ -617,10 +652,13 @@ void grouped_gemm(const GemmParams p) {
           const halfx2 h01 = {static_cast<_Float16>(acc[u][0] * sup), static_cast<_Float16>(acc[u][1] * sup)};
           const halfx2 h23 = {static_cast<_Float16>(acc[u][2] * sup), static_cast<_Float16>(acc[u][3] * sup)};
           const size_t off = static_cast<size_t>(r) * p.out_rows + ng * p.tile_stride + rl + 4 * lq;
-          *reinterpret_cast<uint2*>(p.a16 + off) =
-              make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+          if (nvalid)
+            *reinterpret_cast<uint2*>(p.a16 + off) =
+                make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+          // (Neuron ng * 64 of wave 0, lane group 0, always exists.)
+          const int nslab_out = (p.out_rows + kSlabK - 1) / kSlabK;
           if (wave == 0 && lq == 0)
-            p.a_scale[(static_cast<size_t>(r) * (p.out_rows / kSlabK) + (ng >> 1)) * 4 + (ng & 1)] = pow2f(-t);
+            p.a_scale[(static_cast<size_t>(r) * nslab_out + (ng >> 1)) * 4 + (ng & 1)] = pow2f(-t);
         }
       }
     } else {
@@ -628,7 +666,7 @@ void grouped_gemm(const GemmParams p) {
       for (int u = 0; u < kSub; ++u) {
         if (u >= nact) break;
         const int r = __shfl(rc, 16 * act[u] + n, kWave);
-        if (r < 0) continue;
+        if (r < 0 || (kRagged && ng * p.tile_stride + 64 * rs + rl + 4 * lq >= p.out_rows)) continue;
         const size_t off = static_cast<size_t>(r) * p.out_rows + ng * p.tile_stride + 64 * rs + rl + 4 * lq;
         *reinterpret_cast<float4*>(p.yhat + off) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
       }
@@ -693,6 +731,27 @@ bool group_ok(int K, int g, int slab) {
   return g < slab ? (slab % g) == 0 : (g % slab) == 0;
 }
 
+template <int kFmt, bool kGateUp, bool kSmall, bool kRagged>
+hipError_t launch_gemm_ring_as(const GemmParams& gp, int wgs, uint32_t lds, hipStream_t stream) {
+  if constexpr (kFmt == MOE_W_MXFP8) {
+    launch(grouped_gemm<kFmt, kGateUp, 1, kSmall, kRagged>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
+  } else {
+    switch (flush_steps(gp.g, kSteps)) {
+      case 1:
+        launch(grouped_gemm<kFmt, kGateUp, 1, kSmall, kRagged>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
+        break;
+      case 2:
+        launch(grouped_gemm<kFmt, kGateUp, 2, kSmall, kRagged>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
+        break;
+      default:
+        launch(grouped_gemm<kFmt, kGateUp, kSteps, kSmall, kRagged>, dim3(wgs), dim3(kGemmThreads), lds, stream,
+               gp);
+        break;
+    }
+  }
+  return hipGetLastError();
+}
+
 template <int kFmt, bool kGateUp, bool kSmall>
 hipError_t launch_gemm_ring(const GemmParams& gp_in, int wgs, hipStream_t stream) {
   // The tile's scales (and int4 zeros) for all K / g groups of its two row
@@ -703,22 +762,10 @@ hipError_t launch_gemm_ring(const GemmParams& gp_in, int wgs, hipStream_t stream
   gp.sc_set = (kTileRows * gpr * sc_bytes + 1023) / 1024 * 1024;
   gp.zp_set = kFmt == MOE_W_MXFP8 ? 0 : (kTileRows * gpr + 1023) / 1024 * 1024;
   const uint32_t lds = static_cast<uint32_t>(2 * gp.sc_set + 2 * gp.zp_set);
-  if constexpr (kFmt == MOE_W_MXFP8) {
-    launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
-  } else {
-    switch (flush_steps(gp.g, kSteps)) {
-      case 1:
-        launch(grouped_gemm<kFmt, kGateUp, 1, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
-        break;
-      case 2:
-        launch(grouped_gemm<kFmt, kGateUp, 2, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
-        break;
-      default:
-        launch(grouped_gemm<kFmt, kGateUp, kSteps, kSmall>, dim3(wgs), dim3(kGemmThreads), lds, stream, gp);
-        break;
-    }
-  }
-  return hipGetLastError();
+  // Shapes on the 128 grid take the instantiation without the tail checks.
+  if ((gp.K % kSlabK) != 0 || (gp.out_rows % gp.tile_stride) != 0)
+    return launch_gemm_ring_as<kFmt, kGateUp, kSmall, true>(gp, wgs, lds, stream);
+  return launch_gemm_ring_as<kFmt, kGateUp, kSmall, false>(gp, wgs, lds, stream);
 }
 
 // MXFP8 blocks are 32 elements: one scaled partial per MFMA step. Layers
@@ -738,10 +785,11 @@ hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t strea
 }  // namespace
 
 bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2) {
-  // Whole slabs and whole tiles in both GEMMs (gate/up: 64 neurons; down:
-  // 128 rows; 128-element slabs); the tile's scales (and int4 zeros) are
-  // staged in LDS: at most 128 groups (int4) or blocks of 32 (MXFP8) per row.
-  if (b < 1 || b > kMaxTok || (H % kSlabK) != 0 || (I % kSlabK) != 0) return false;
+  // H and I multiples of 32 (one MFMA step): the last tile of a GEMM may be
+  // partly outside the output rows and the last slab shorter than 128; the
+  // tile's scales (and int4 zeros) are staged in LDS: at most 128 groups
+  // (int4) or blocks of 32 (MXFP8) per row.
+  if (b < 1 || b > kMaxTok || H < 32 || I < 32 || (H % 32) != 0 || (I % 32) != 0) return false;
   if (fmt == MOE_W_MXFP8) return g13 == 32 && g2 == 32 && H / 32 <= kMaxGpr && I / 32 <= kMaxGpr;
   return group_ok(H, g13, kSlabK) && group_ok(I, g2, kSlabK);
 }
@@ -763,7 +811,7 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.E = p.E;
   gp.b = p.b;
   gp.nblk = p.nblk;
-  gp.ntile = p.I / kTileRows;
+  gp.ntile = (p.I + kTileRows - 1) / kTileRows;
   gp.rows_per_expert = 2 * p.I;
   gp.set_stride = p.I;
   gp.tile_stride = kTileRows;
@@ -790,7 +838,7 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.E = p.E;
   gp.b = p.b;
   gp.nblk = p.nblk;
-  gp.ntile = p.H / (2 * kTileRows);
+  gp.ntile = (p.H + 2 * kTileRows - 1) / (2 * kTileRows);
   gp.rows_per_expert = p.H;
   gp.set_stride = kTileRows;
   gp.tile_stride = 2 * kTileRows;
@@ -817,7 +865,7 @@ hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* c
   gp.E = p.E;
   gp.b = p.b;
   gp.nblk = p.E * gp.nbpe;
-  gp.ntile = p.I / kTileRows;
+  gp.ntile = (p.I + kTileRows - 1) / kTileRows;
   gp.rows_per_expert = 2 * p.I;
   gp.set_stride = p.I;
   gp.tile_stride = kTileRows;
@@ -844,7 +892,7 @@ hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* coun
   gp.E = p.E;
   gp.b = p.b;
   gp.nblk = p.E * gp.nbpe;
-  gp.ntile = p.H / (2 * kTileRows);
+  gp.ntile = (p.H + 2 * kTileRows - 1) / (2 * kTileRows);
   gp.rows_per_expert = p.H;
   gp.set_stride = kTileRows;
   gp.tile_stride = 2 * kTileRows;

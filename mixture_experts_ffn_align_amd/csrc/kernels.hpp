@@ -83,7 +83,7 @@ struct GroupedArgs {
   const int32_t* num_padded;
   moe_weights w13, w2;
   uint16_t* a16;   // fp16 [M*k][I] intermediate, each 64-neuron chunk of a route scaled by a power of two
-  float* a_scale;  // fp32 [M*k][I/128][4]: entries 0 and 1 undo the scaling of the slab's two chunks
+  float* a_scale;  // fp32 [M*k][ceil(I/128)][4]: entries 0 and 1 undo the scaling of the slab's two chunks
   float* yhat;     // fp32 [M*k][H]
   float* w13_out;  // fp32 [M*k][2I] W13 outputs (gate, up) or null: capture surface
   float* y;        // fp32 [M][H]

@@ -25,15 +25,16 @@ INTERMEDIATE_REL_L2 = {1: 1e-4, 2: 2.0 ** -11 + 1e-5}
 
 def decode_scaled_f16(a16, mult):
     """Format-2 intermediate as fp64: a16 [..., I] fp16 values and mult
-    [..., I/128, 4] fp32, entries 0 and 1 of slab s multiplying the elements
-    of chunks 2s and 2s+1 (64 elements each)."""
+    [..., ceil(I/128), 4] fp32, entries 0 and 1 of slab s multiplying the
+    elements of chunks 2s and 2s+1 (64 elements each; the last chunk may be
+    partial)."""
     # Rows the library leaves unspecified (invalid routes) and the unused
     # entries may hold any bits, signalling NaNs included.
     with np.errstate(invalid="ignore"):
         a = np.asarray(a16).astype(np.float64)
         m = np.asarray(mult)[..., :2].astype(np.float64)
-        m = m.reshape(m.shape[:-2] + (a.shape[-1] // 64,))
-        return a * np.repeat(m, 64, axis=-1)
+        m = m.reshape(m.shape[:-2] + (2 * m.shape[-2],))
+        return a * np.repeat(m, 64, axis=-1)[..., :a.shape[-1]]
 
 
 def alignment_mismatch(got, ref):

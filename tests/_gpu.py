@@ -57,7 +57,8 @@ class DeviceWorkload:
         else:
             assert fmt == 2, fmt
             a16 = ws[off:off + 2 * n].view(torch.float16).reshape(mk, I).cpu().numpy()
-            mult = ws[aux:aux + 16 * mk * (I // 128)].view(torch.float32).reshape(mk, I // 128, 4).cpu().numpy()
+            ns = -(-I // 128)
+            mult = ws[aux:aux + 16 * mk * ns].view(torch.float32).reshape(mk, ns, 4).cpu().numpy()
             a = decode_scaled_f16(a16, mult)
         return a, fmt
 

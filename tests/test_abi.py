@@ -147,8 +147,12 @@ def test_auto_path_threshold():
     assert rp(_desc(M=1, k=20)) == B.MOE_PATH_GROUPED              # decode: at most 16 routes per token
     assert rp(_desc(M=1, g13=256, g2=256, I=768, H=2048)) == B.MOE_PATH_DECODE
     assert rp(_desc(M=1, k=20, path=B.MOE_PATH_DECODE)) == -1
-    assert rp(_desc(M=64, I=448, g2=64)) == B.MOE_PATH_DECODE      # grouped: I a multiple of 128
-    assert rp(_desc(M=64, I=448, g2=64, path=B.MOE_PATH_GROUPED)) == -1
+    assert rp(_desc(M=64, b=128)) == B.MOE_PATH_DECODE              # grouped: blocks of at most 64 routes
+    assert rp(_desc(M=64, b=128, path=B.MOE_PATH_GROUPED)) == -1
+    # Both paths take H and I that are multiples of 32 only.
+    assert rp(_desc(M=64, I=448, g2=64)) == B.MOE_PATH_GROUPED
+    assert rp(_desc(M=64, H=2080, I=160, g13=32, g2=32)) == B.MOE_PATH_GROUPED
+    assert rp(_desc(M=64, H=2080, I=176, g13=32, g2=32, path=B.MOE_PATH_GROUPED)) == -1
     assert rp(_desc(M=-1)) == -1
 
 

@@ -92,11 +92,20 @@ RAGGED = [
     dict(M=70, H=1024, I=256, E=16, k=6, b=64, g=32, fmt="mxfp8"),
     # Decode gate/up with more than one 32-element chunk per lane (H/32 > 64):
     # a whole second chunk (H = 4096) and one lane with a second chunk
-    # (H = 2080; the grouped path needs H a multiple of 128), both formats.
+    # (H = 2080, on the grouped path a gate/up reduction that ends in a
+    # one-step slab), both formats.
     dict(M=2, H=4096, I=256, E=8, k=4, b=8, g=128),
     dict(M=3, H=2080, I=128, E=8, k=2, b=8, g=32),
     dict(M=2, H=4096, I=256, E=8, k=4, b=8, g=32, fmt="mxfp8"),
     dict(M=3, H=2080, I=128, E=8, k=2, b=8, g=32, fmt="mxfp8"),
+    # Grouped GEMMs whose last tile is partly outside the output rows and
+    # whose last slab is shorter than 128 (H and I off the 128 grid), over
+    # several blocks: down tiles of 64 / 32 valid rows, gate/up tiles of 32
+    # valid neurons, last slabs of one, two and three steps, both formats.
+    dict(M=40, H=192, I=160, E=8, k=2, b=64, g=32),
+    dict(M=33, H=2080, I=96, E=16, k=4, b=16, g=32),
+    dict(M=60, H=448, I=320, E=8, k=2, b=48, g=64),
+    dict(M=50, H=352, I=224, E=8, k=3, b=32, g=32, fmt="mxfp8"),
     # The grouped small-block variant (int4, b <= 16, groups of 128 or
     # more, K <= 2048): nine gate/up slabs (the weight-load window refills
     # once), fifteen down slabs, and blocks filled to all 16 columns.
@@ -127,8 +136,8 @@ RAGGED = [
 
 def _sampled_shapes(n, seed):
     """Seeded random layer shapes inside what the library takes (decode: H and
-    I multiples of 32, power-of-two groups, k <= 16; grouped: H and I
-    multiples of 128, b <= 64, at most 128 groups per row), both weight
+    I multiples of 32, power-of-two groups, k <= 16; grouped: b <= 64, at
+    most 128 groups per row), both weight
     formats, block sizes that are not multiples of 16 among them, sized so
     that the oracle takes about a second or less per shape."""
     rng = np.random.default_rng(seed)
@@ -288,10 +297,11 @@ def test_auto_path_falls_back_to_grouped():
 
 
 def test_auto_path_falls_back_to_decode():
-    # I = 448 is not a multiple of 128, which the grouped path needs: the
-    # automatic path runs the decode path even at M = 20, and matches the oracle.
+    # Blocks of 128 routes are more than the grouped path's tiles take (64):
+    # the automatic path runs the decode path even at M = 20, and matches the
+    # oracle.
     g = _gpu()
-    wl = _custom(14, M=20, H=256, I=448, E=16, k=4, b=16, g=64)
+    wl = _custom(14, M=20, H=256, I=448, E=16, k=4, b=128, g=64)
     dw = g.DeviceWorkload(wl)
     assert moe.moe_ffn_resolved_path(dw.layer.desc(20, moe.MOE_PATH_AUTO)) == moe.MOE_PATH_DECODE
     ref = oracle.ffn(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
