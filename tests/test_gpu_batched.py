@@ -30,7 +30,7 @@ def _run(layer, xb_np, counts_np, E, cap, I, H):
     xb = torch.from_numpy(xb_np.view(np.int16)).cuda().view(torch.bfloat16)
     counts = torch.from_numpy(np.asarray(counts_np, dtype=np.int32)).cuda()
     a16 = torch.full((E, cap, I), float("nan"), dtype=torch.float16, device="cuda")
-    mult = torch.full((E, cap, I // 128, 4), float("nan"), dtype=torch.float32, device="cuda")
+    mult = torch.full((E, cap, -(-I // 128), 4), float("nan"), dtype=torch.float32, device="cuda")
     yb = torch.full((E, cap, H), float("nan"), dtype=torch.float32, device="cuda")
     d = layer.desc(1)
     moe.moe_ffn_gate_up_batched(d, xb, counts, a16, mult)
@@ -49,6 +49,10 @@ SHAPES = [
     # 16-row tiles, an empty expert and a count past the capacity.
     dict(E=6, cap=37, H=1024, I=384, b=16, g=128, counts=[37, 0, 5, 16, 17, 40], fmt="int4"),
     dict(E=4, cap=9, H=256, I=128, b=8, g=128, counts=[9, 3, 0, 12], fmt="int4"),
+    # H and I off the 128 grid: partial last tiles, short last slabs.
+    dict(E=4, cap=20, H=320, I=160, b=16, g=32, counts=[20, 7, 0, 13], fmt="int4"),
+    dict(E=3, cap=50, H=2080, I=96, b=64, g=32, counts=None, fmt="int4"),
+    dict(E=3, cap=30, H=352, I=224, b=32, g=32, counts=[30, 17, 1], fmt="mxfp8"),
 ]
 
 

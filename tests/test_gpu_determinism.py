@@ -163,3 +163,26 @@ def test_decode_wide_hidden_repeats_and_caps(fmt, g, H):
         assert digest(dw.forward(moe.MOE_PATH_DECODE).cpu().numpy()) == ref
     for cap in (1, 7, 100):
         assert digest(dw.forward(moe.MOE_PATH_DECODE, max_workgroups=cap).cpu().numpy()) == ref
+
+
+@pytest.mark.parametrize("fmt,g,H,I", [("int4", 32, 2080, 96), ("int4", 64, 448, 320), ("mxfp8", 32, 352, 224)])
+def test_grouped_ragged_repeats_caps_and_batch(fmt, g, H, I):
+    # The grouped GEMMs' tail handling (partial last tiles, short last
+    # slabs): repeats and workgroup caps leave every output byte unchanged,
+    # and each token alone gives its row of the batch bitwise.
+    import dataclasses
+    from workloads import CONFIGS, make_workload
+    gpu = _gpu()
+    cfg = dataclasses.replace(CONFIGS["tiny"], name="ragged", M=40, H=H, I=I, E=8, k=2, b=16, g=g, fmt=fmt)
+    wl = make_workload(cfg, seed=23)
+    dw = gpu.DeviceWorkload(wl)
+    gpu.announce("grouped-ragged", fmt, H, I)
+    y = dw.forward(moe.MOE_PATH_GROUPED).cpu().numpy()
+    ref = digest(y)
+    for _ in range(3):
+        assert digest(dw.forward(moe.MOE_PATH_GROUPED).cpu().numpy()) == ref
+    for cap in (1, 7, 100):
+        assert digest(dw.forward(moe.MOE_PATH_GROUPED, max_workgroups=cap).cpu().numpy()) == ref
+    for t in (0, 17, 39):
+        yt = dw.forward(moe.MOE_PATH_GROUPED, x=dw.x[t:t + 1], ids=dw.ids[t:t + 1], w=dw.w[t:t + 1])
+        assert digest(yt.cpu().numpy()[0]) == digest(y[t]), t
