@@ -73,8 +73,9 @@ typedef enum {
                             chosen path's shape rules fail, the other path */
   MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
   MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised MFMA grouped GEMMs + combine; needs H and I
-                            multiples of 32 (as every path), b <= 64, at most 128 scale groups
-                            per row (K/group; MXFP8: K/32) and (int4) group dividing 128 or a
+                            multiples of 32 (as every path), b <= 64, at most 256 scale groups
+                            per row (K/group; MXFP8: K/32) whose scales and zeros fit one CU's
+                            LDS beside the tile's ring, and (int4) group dividing 128 or a
                             multiple of it */
 } moe_path;
 

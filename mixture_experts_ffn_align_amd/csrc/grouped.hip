@@ -62,7 +62,8 @@ constexpr int kThreads = 256;            // combine workgroup
 constexpr int kTileRows = 64;            // weight rows per row set of a GEMM tile (four waves of 16)
 constexpr int kMaxTok = 64;              // block size limit: four 16-column sub-tiles
 constexpr int kMaxSub = kMaxTok / 16;
-constexpr int kMaxGpr = 128;             // K / g limit (the tile's scales live in LDS)
+constexpr int kMaxGpr = 256;             // K / g limit (the tile's scales live in LDS; see lds_fits)
+constexpr int kLdsPerCu = 160 * 1024;
 
 constexpr int kSteps = 4;                // 32-element MFMA steps per slab
 constexpr int kSlabK = 32 * kSteps;      // reduction elements per slab
@@ -726,6 +727,26 @@ __global__ __launch_bounds__(kThreads) void combine_topk(
 // (g a multiple of the slab).
 int flush_steps(int g, int steps) { return g >= 32 * steps ? steps : g / 32; }
 
+// LDS bytes per row set of a tile's scales and (int4) zeros: all K / g
+// groups of 64 rows, rounded up to whole 1 KB DMA pieces.
+int scale_set_bytes(int fmt, int gpr) { return (kTileRows * gpr * (fmt == MOE_W_MXFP8 ? 1 : 2) + 1023) / 1024 * 1024; }
+int zero_set_bytes(int fmt, int gpr) { return fmt == MOE_W_MXFP8 ? 0 : (kTileRows * gpr + 1023) / 1024 * 1024; }
+
+// One workgroup's LDS (its ring and both row sets' scales and zeros) fits a
+// CU: above 128 groups per row only one workgroup per CU does.
+template <int kFmt, bool kGateUp, bool kSmall>
+bool lds_fits_as(int gpr) {
+  return Ring<kFmt, kGateUp, kSmall>::kBytes + 2 * scale_set_bytes(kFmt, gpr) + 2 * zero_set_bytes(kFmt, gpr) <=
+         kLdsPerCu;
+}
+
+template <bool kGateUp>
+bool lds_fits(int fmt, int b, int gpr) {
+  if (fmt == MOE_W_MXFP8)
+    return b <= 16 ? lds_fits_as<MOE_W_MXFP8, kGateUp, true>(gpr) : lds_fits_as<MOE_W_MXFP8, kGateUp, false>(gpr);
+  return b <= 16 ? lds_fits_as<MOE_W_INT4_AWQ, kGateUp, true>(gpr) : lds_fits_as<MOE_W_INT4_AWQ, kGateUp, false>(gpr);
+}
+
 bool group_ok(int K, int g, int slab) {
   if (g < 32 || (g % 32) != 0 || (K % g) != 0 || K / g > kMaxGpr) return false;
   return g < slab ? (slab % g) == 0 : (g % slab) == 0;
@@ -758,9 +779,8 @@ hipError_t launch_gemm_ring(const GemmParams& gp_in, int wgs, hipStream_t stream
   // sets, each set rounded up to whole 1 KB DMA pieces.
   GemmParams gp = gp_in;
   const int gpr = gp.K / gp.g;
-  const int sc_bytes = kFmt == MOE_W_MXFP8 ? 1 : 2;
-  gp.sc_set = (kTileRows * gpr * sc_bytes + 1023) / 1024 * 1024;
-  gp.zp_set = kFmt == MOE_W_MXFP8 ? 0 : (kTileRows * gpr + 1023) / 1024 * 1024;
+  gp.sc_set = scale_set_bytes(kFmt, gpr);
+  gp.zp_set = zero_set_bytes(kFmt, gpr);
   const uint32_t lds = static_cast<uint32_t>(2 * gp.sc_set + 2 * gp.zp_set);
   // Shapes on the 128 grid take the instantiation without the tail checks.
   if ((gp.K % kSlabK) != 0 || (gp.out_rows % gp.tile_stride) != 0)
@@ -787,11 +807,15 @@ hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t strea
 bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2) {
   // H and I multiples of 32 (one MFMA step): the last tile of a GEMM may be
   // partly outside the output rows and the last slab shorter than 128; the
-  // tile's scales (and int4 zeros) are staged in LDS: at most 128 groups
-  // (int4) or blocks of 32 (MXFP8) per row.
+  // tile's scales (and int4 zeros) are staged in LDS: at most 256 groups
+  // (int4) or blocks of 32 (MXFP8) per row, within one CU's LDS.
   if (b < 1 || b > kMaxTok || H < 32 || I < 32 || (H % 32) != 0 || (I % 32) != 0) return false;
-  if (fmt == MOE_W_MXFP8) return g13 == 32 && g2 == 32 && H / 32 <= kMaxGpr && I / 32 <= kMaxGpr;
-  return group_ok(H, g13, kSlabK) && group_ok(I, g2, kSlabK);
+  if (fmt == MOE_W_MXFP8) {
+    if (g13 != 32 || g2 != 32 || H / 32 > kMaxGpr || I / 32 > kMaxGpr) return false;
+  } else if (!group_ok(H, g13, kSlabK) || !group_ok(I, g2, kSlabK)) {
+    return false;
+  }
+  return lds_fits<true>(fmt, b, H / g13) && lds_fits<false>(fmt, b, I / g2);
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {

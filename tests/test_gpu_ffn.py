@@ -106,15 +106,20 @@ RAGGED = [
     dict(M=33, H=2080, I=96, E=16, k=4, b=16, g=32),
     dict(M=60, H=448, I=320, E=8, k=2, b=48, g=64),
     dict(M=50, H=352, I=224, E=8, k=3, b=32, g=32, fmt="mxfp8"),
+    # More than 128 groups per row on the grouped path (256: one workgroup
+    # per CU, the four-sub-tile int4 kernel at exactly a CU's 160 KB of LDS).
+    dict(M=40, H=8192, I=256, E=4, k=2, b=64, g=32),
+    dict(M=20, H=8192, I=256, E=4, k=2, b=16, g=32),
+    dict(M=30, H=8192, I=384, E=4, k=2, b=32, g=32, fmt="mxfp8"),
     # The grouped small-block variant (int4, b <= 16, groups of 128 or
     # more, K <= 2048): nine gate/up slabs (the weight-load window refills
     # once), fifteen down slabs, and blocks filled to all 16 columns.
     dict(M=11, H=1152, I=384, E=16, k=4, b=8, g=128),
     dict(M=7, H=2048, I=1920, E=8, k=3, b=16, g=128),
     dict(M=33, H=640, I=256, E=4, k=2, b=16, g=128),
-    # Up to 128 scale groups per row on the grouped path (the tile's scales
-    # are staged in LDS sized per launch): int4 g = 32 at H = 2048 (64
-    # groups), H = 4096 (128 groups), and MXFP8 at H = 4096 (128 blocks).
+    # Many scale groups per row on the grouped path (the tile's scales are
+    # staged in LDS sized per launch): int4 g = 32 at H = 2048 (64 groups),
+    # H = 4096 (128 groups), and MXFP8 at H = 4096 (128 blocks).
     dict(M=40, H=2048, I=256, E=8, k=2, b=16, g=32),
     dict(M=48, H=4096, I=256, E=8, k=2, b=64, g=32),
     dict(M=40, H=4096, I=256, E=8, k=2, b=16, g=32, fmt="mxfp8"),
@@ -137,7 +142,7 @@ RAGGED = [
 def _sampled_shapes(n, seed):
     """Seeded random layer shapes inside what the library takes (decode: H and
     I multiples of 32, power-of-two groups, k <= 16; grouped: b <= 64, at
-    most 128 groups per row), both weight
+    most 256 groups per row), both weight
     formats, block sizes that are not multiples of 16 among them, sized so
     that the oracle takes about a second or less per shape."""
     rng = np.random.default_rng(seed)
