@@ -73,7 +73,7 @@ typedef enum {
                             chosen path's shape rules fail, the other path */
   MOE_PATH_DECODE = 1,   /* output-stationary: one wave64 per output neuron set, no alignment */
   MOE_PATH_GROUPED = 2   /* alignment + LDS-dequantised MFMA grouped GEMMs + combine; needs H and I
-                            multiples of 32 (as every path), b <= 64, at most 256 scale groups
+                            multiples of 32 (as every path), b <= 1024, at most 256 scale groups
                             per row (K/group; MXFP8: K/32) whose scales and zeros fit one CU's
                             LDS beside the tile's ring, and (int4) group dividing 128 or a
                             multiple of it */
@@ -97,7 +97,7 @@ typedef struct {
   int32_t E;               /* experts held here (1..2048): IDs expert_base .. expert_base + E - 1 */
   int32_t k;               /* routes per token (>= 1) */
   int32_t b;               /* alignment block size used by the grouped path (>= 1; the
-                              grouped GEMMs take b <= 64) */
+                              grouped GEMMs take b <= 1024, in parts of up to 64 routes) */
   moe_weights w13;
   moe_weights w2;
   int32_t path;            /* moe_path */

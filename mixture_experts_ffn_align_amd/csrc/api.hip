@@ -71,7 +71,8 @@ bool shape_ok(int path, const moe_ffn_desc* d) {
 bool tasks_fit(int path, const moe_ffn_desc* d, int64_t mk) {
   const int64_t M = d->M, H = d->H, I = d->I;
   if (path == MOE_PATH_DECODE) return mk * (I / 2) <= kMaxTasks && M * (H / 8) <= kMaxTasks;
-  const int64_t nblk = static_cast<int64_t>(capacity_of(d->M, d->k, d->E, d->b)) / d->b;
+  // Blocks of 64-column parts (blocks above 64 routes take several).
+  const int64_t nblk = static_cast<int64_t>(capacity_of(d->M, d->k, d->E, d->b)) / d->b * ((d->b + 63) / 64);
   if (M * (H / 4) > kMaxTasks) return false;
   return nblk * ((I + 63) / 64) <= kMaxTasks && nblk * ((H + 127) / 128) <= kMaxTasks;
 }
@@ -444,7 +445,7 @@ moe_status validate_batched(const moe_ffn_desc* d, int32_t capacity) {
   if (st != MOE_OK) return st;
   if (int64_t(d->E) * capacity > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   // GEMM tasks: E * ceil(capacity / b) blocks times the tiles per block.
-  const int64_t nblk = int64_t(d->E) * ((int64_t(capacity) + d->b - 1) / d->b);
+  const int64_t nblk = int64_t(d->E) * ((int64_t(capacity) + d->b - 1) / d->b) * ((d->b + 63) / 64);
   if (nblk * ((d->I + 63) / 64) > kMaxTasks || nblk * ((d->H + 127) / 128) > kMaxTasks) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -60,7 +60,9 @@ namespace {
 
 constexpr int kThreads = 256;            // combine workgroup
 constexpr int kTileRows = 64;            // weight rows per row set of a GEMM tile (four waves of 16)
-constexpr int kMaxTok = 64;              // block size limit: four 16-column sub-tiles
+constexpr int kMaxTok = 64;              // columns per task: four 16-column sub-tiles (a larger
+                                         // block is split into parts of 64 columns)
+constexpr int kMaxBlock = 1024;          // block size limit
 constexpr int kMaxSub = kMaxTok / 16;
 constexpr int kMaxGpr = 256;             // K / g limit (the tile's scales live in LDS; see lds_fits)
 constexpr int kLdsPerCu = 160 * 1024;
@@ -189,7 +191,8 @@ struct GemmParams {
   float* yhat;                   // down output [Mk][H]
   float* w13_out;                // gate/up: fp32 [Mk][2I] W13 outputs (gate, up) or null
   int mk, k, E, b, nblk;
-  int ntile;                     // tiles per block
+  int ntile;                     // weight tiles per part of a block
+  int nparts;                    // 64-column parts per block, ceil(b / 64)
   int rows_per_expert;           // weight rows per expert (2I or H)
   int set_stride;                // row offset of row set 1 (I: up rows; 64: next 64 rows)
   int tile_stride;               // row offset between tiles (64 or 128)
@@ -257,7 +260,8 @@ void grouped_gemm(const GemmParams p) {
   const int rs = wave >> 2;                         // this wave's row set
   const int rl = 16 * (wave & 3);                   // first row of this wave within the set
   const int n = lane & 15, lq = lane >> 4;
-  const int ntasks = p.nblk * p.ntile;
+  const int per_blk = p.nparts * p.ntile;              // tasks per block
+  const int ntasks = p.nblk * per_blk;
   const bool batched = p.counts != nullptr;
   const int npad = batched ? 0 : p.num_padded[0];
   const int row_bytes = kMx ? p.K : p.K / 2, gpr = p.K / p.g;
@@ -270,8 +274,12 @@ void grouped_gemm(const GemmParams p) {
   const uint32_t nib_mask = in_vgpr(kNibMask<kHalf>);
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-    const int blk = task / p.ntile;
-    const int ng = task - blk * p.ntile;
+    const int bp = task / p.ntile;                        // (block, part) index
+    const int ng = task - bp * p.ntile;
+    const int blk = p.nparts == 1 ? bp : bp / p.nparts;
+    const int part = bp - blk * p.nparts;                 // 64-column part of the block
+    const int cb = part * kMaxTok;                        // its first column within the block
+    const int bw = min(p.b - cb, kMaxTok);                // and its columns
     // Every wave holds the block's columns itself, lane c column c (b <= 64):
     // rc is its route (batched layout: its row), -1 for padding, and bc the
     // B row it reads. The expert ID and the routes are loaded together, and
@@ -284,12 +292,12 @@ void grouped_gemm(const GemmParams p) {
       e = blk / p.nbpe;
       const int j = blk - e * p.nbpe;
       const int cnt = min(max(p.counts[e], 0), p.cap);
-      if (j * p.b >= cnt) continue;
-      if (lane < min(p.b, cnt - j * p.b)) rc = e * p.cap + j * p.b + lane;
+      if (j * p.b + cb >= cnt) continue;
+      if (lane < min(bw, cnt - j * p.b - cb)) rc = e * p.cap + j * p.b + cb + lane;
     } else {
       if (blk * p.b >= npad) continue;
       // blk < nblk keeps the index inside the alignment's capacity.
-      const int rr = lane < p.b ? p.sorted[static_cast<size_t>(blk) * p.b + lane] : -1;
+      const int rr = lane < bw ? p.sorted[static_cast<size_t>(blk) * p.b + cb + lane] : -1;
       e = p.blocks[blk];
       if (e < 0 || e >= p.E) continue;
       rc = (rr >= 0 && rr < p.mk) ? rr : -1;
@@ -809,7 +817,7 @@ bool grouped_shape_ok(int fmt, int H, int I, int b, int g13, int g2) {
   // partly outside the output rows and the last slab shorter than 128; the
   // tile's scales (and int4 zeros) are staged in LDS: at most 256 groups
   // (int4) or blocks of 32 (MXFP8) per row, within one CU's LDS.
-  if (b < 1 || b > kMaxTok || H < 32 || I < 32 || (H % 32) != 0 || (I % 32) != 0) return false;
+  if (b < 1 || b > kMaxBlock || H < 32 || I < 32 || (H % 32) != 0 || (I % 32) != 0) return false;
   if (fmt == MOE_W_MXFP8) {
     if (g13 != 32 || g2 != 32 || H / 32 > kMaxGpr || I / 32 > kMaxGpr) return false;
   } else if (!group_ok(H, g13, kSlabK) || !group_ok(I, g2, kSlabK)) {
@@ -836,13 +844,14 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.b = p.b;
   gp.nblk = p.nblk;
   gp.ntile = (p.I + kTileRows - 1) / kTileRows;
+  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = 2 * p.I;
   gp.set_stride = p.I;
   gp.tile_stride = kTileRows;
   gp.out_rows = p.I;
   gp.K = p.H;
   gp.g = p.w13.group;
-  const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
   return launch_gemm<true>(p.w13.fmt, gp, wgs, stream);
 }
 
@@ -863,13 +872,14 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.b = p.b;
   gp.nblk = p.nblk;
   gp.ntile = (p.H + 2 * kTileRows - 1) / (2 * kTileRows);
+  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = p.H;
   gp.set_stride = kTileRows;
   gp.tile_stride = 2 * kTileRows;
   gp.out_rows = p.H;
   gp.K = p.I;
   gp.g = p.w2.group;
-  const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
   return launch_gemm<false>(p.w2.fmt, gp, wgs, stream);
 }
 
@@ -890,13 +900,14 @@ hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* c
   gp.b = p.b;
   gp.nblk = p.E * gp.nbpe;
   gp.ntile = (p.I + kTileRows - 1) / kTileRows;
+  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = 2 * p.I;
   gp.set_stride = p.I;
   gp.tile_stride = kTileRows;
   gp.out_rows = p.I;
   gp.K = p.H;
   gp.g = p.w13.group;
-  const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(gp.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
   return launch_gemm<true>(p.w13.fmt, gp, wgs, stream);
 }
 
@@ -917,13 +928,14 @@ hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* coun
   gp.b = p.b;
   gp.nblk = p.E * gp.nbpe;
   gp.ntile = (p.H + 2 * kTileRows - 1) / (2 * kTileRows);
+  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = p.H;
   gp.set_stride = kTileRows;
   gp.tile_stride = 2 * kTileRows;
   gp.out_rows = p.H;
   gp.K = p.I;
   gp.g = p.w2.group;
-  const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(gp.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
   return launch_gemm<false>(p.w2.fmt, gp, wgs, stream);
 }
 

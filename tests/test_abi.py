@@ -147,8 +147,9 @@ def test_auto_path_threshold():
     assert rp(_desc(M=1, k=20)) == B.MOE_PATH_GROUPED              # decode: at most 16 routes per token
     assert rp(_desc(M=1, g13=256, g2=256, I=768, H=2048)) == B.MOE_PATH_DECODE
     assert rp(_desc(M=1, k=20, path=B.MOE_PATH_DECODE)) == -1
-    assert rp(_desc(M=64, b=128)) == B.MOE_PATH_DECODE              # grouped: blocks of at most 64 routes
-    assert rp(_desc(M=64, b=128, path=B.MOE_PATH_GROUPED)) == -1
+    assert rp(_desc(M=64, b=2048)) == B.MOE_PATH_DECODE             # grouped: blocks of at most 1024 routes
+    assert rp(_desc(M=64, b=2048, path=B.MOE_PATH_GROUPED)) == -1
+    assert rp(_desc(M=64, b=128)) == B.MOE_PATH_GROUPED               # in two parts of 64 columns
     # Both paths take H and I that are multiples of 32 only.
     assert rp(_desc(M=64, I=448, g2=64)) == B.MOE_PATH_GROUPED
     assert rp(_desc(M=64, H=2080, I=160, g13=32, g2=32)) == B.MOE_PATH_GROUPED
@@ -174,7 +175,7 @@ def test_desc_validation():
     assert _ws_status(_desc(q=FAKE + 4)) == B.MOE_ERR_INVALID_ARG  # weights not 16-byte aligned
     assert _ws_status(_desc(path=7)) == B.MOE_ERR_INVALID_ARG
     assert _ws_status(_desc(E=4096, k=8)) == B.MOE_ERR_UNSUPPORTED
-    assert _ws_status(_desc(M=256, b=128, path=B.MOE_PATH_GROUPED)) == B.MOE_ERR_UNSUPPORTED
+    assert _ws_status(_desc(M=256, b=2048, path=B.MOE_PATH_GROUPED)) == B.MOE_ERR_UNSUPPORTED
     # Layers whose kernels would exceed 2^30 tasks are refused, not truncated.
     assert _ws_status(_desc(M=2**21, path=B.MOE_PATH_DECODE)) == B.MOE_ERR_UNSUPPORTED
     assert _ws_status(_desc(M=2**21, H=2**14, I=2**14, g13=512, g2=512, b=1,

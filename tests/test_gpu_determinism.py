@@ -165,15 +165,16 @@ def test_decode_wide_hidden_repeats_and_caps(fmt, g, H):
         assert digest(dw.forward(moe.MOE_PATH_DECODE, max_workgroups=cap).cpu().numpy()) == ref
 
 
-@pytest.mark.parametrize("fmt,g,H,I", [("int4", 32, 2080, 96), ("int4", 64, 448, 320), ("mxfp8", 32, 352, 224)])
-def test_grouped_ragged_repeats_caps_and_batch(fmt, g, H, I):
+@pytest.mark.parametrize("fmt,g,H,I,b", [("int4", 32, 2080, 96, 16), ("int4", 64, 448, 320, 16),
+                                          ("mxfp8", 32, 352, 224, 16), ("int4", 32, 320, 160, 96)])
+def test_grouped_ragged_repeats_caps_and_batch(fmt, g, H, I, b):
     # The grouped GEMMs' tail handling (partial last tiles, short last
     # slabs): repeats and workgroup caps leave every output byte unchanged,
     # and each token alone gives its row of the batch bitwise.
     import dataclasses
     from workloads import CONFIGS, make_workload
     gpu = _gpu()
-    cfg = dataclasses.replace(CONFIGS["tiny"], name="ragged", M=40, H=H, I=I, E=8, k=2, b=16, g=g, fmt=fmt)
+    cfg = dataclasses.replace(CONFIGS["tiny"], name="ragged", M=40, H=H, I=I, E=8, k=2, b=b, g=g, fmt=fmt)
     wl = make_workload(cfg, seed=23)
     dw = gpu.DeviceWorkload(wl)
     gpu.announce("grouped-ragged", fmt, H, I)

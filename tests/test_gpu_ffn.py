@@ -111,6 +111,11 @@ RAGGED = [
     dict(M=40, H=8192, I=256, E=4, k=2, b=64, g=32),
     dict(M=20, H=8192, I=256, E=4, k=2, b=16, g=32),
     dict(M=30, H=8192, I=384, E=4, k=2, b=32, g=32, fmt="mxfp8"),
+    # Blocks above 64 routes, taken in parts of 64 columns (128 = two whole
+    # parts, 96 = a whole and a half part, 200 = three and a partial one).
+    dict(M=200, H=256, I=128, E=4, k=2, b=128, g=64),
+    dict(M=150, H=320, I=160, E=3, k=2, b=96, g=32),
+    dict(M=120, H=512, I=256, E=2, k=2, b=200, g=32, fmt="mxfp8"),
     # The grouped small-block variant (int4, b <= 16, groups of 128 or
     # more, K <= 2048): nine gate/up slabs (the weight-load window refills
     # once), fifteen down slabs, and blocks filled to all 16 columns.
@@ -141,7 +146,7 @@ RAGGED = [
 
 def _sampled_shapes(n, seed):
     """Seeded random layer shapes inside what the library takes (decode: H and
-    I multiples of 32, power-of-two groups, k <= 16; grouped: b <= 64, at
+    I multiples of 32, power-of-two groups, k <= 16; grouped: b <= 1024, at
     most 256 groups per row), both weight
     formats, block sizes that are not multiples of 16 among them, sized so
     that the oracle takes about a second or less per shape."""
@@ -302,11 +307,11 @@ def test_auto_path_falls_back_to_grouped():
 
 
 def test_auto_path_falls_back_to_decode():
-    # Blocks of 128 routes are more than the grouped path's tiles take (64):
-    # the automatic path runs the decode path even at M = 20, and matches the
+    # Blocks of 2048 routes are more than the grouped path takes (1024): the
+    # automatic path runs the decode path even at M = 20, and matches the
     # oracle.
     g = _gpu()
-    wl = _custom(14, M=20, H=256, I=448, E=16, k=4, b=128, g=64)
+    wl = _custom(14, M=20, H=256, I=448, E=16, k=4, b=2048, g=64)
     dw = g.DeviceWorkload(wl)
     assert moe.moe_ffn_resolved_path(dw.layer.desc(20, moe.MOE_PATH_AUTO)) == moe.MOE_PATH_DECODE
     ref = oracle.ffn(wl.x, wl.topk_ids, wl.topk_w, wl.w13, wl.w2, wl.cfg.E)
