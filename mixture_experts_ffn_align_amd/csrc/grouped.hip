@@ -5,9 +5,10 @@
 // Section 3.4: grouped GEMM over routing-dependent token counts, weights as
 // the left operand so Y_e^T = W_e X_e^T).
 //
-// One kernel template serves both GEMMs. A workgroup of eight waves takes one
-// aligned block (b <= 64 routes of one expert: up to four 16-column
-// sub-tiles) and a tile of two row sets of 64 weight rows (gate/up: the gate
+// One kernel template serves both GEMMs. A workgroup of eight waves takes up
+// to 64 routes of one aligned block (one expert; up to four 16-column
+// sub-tiles; a block of b > 64 routes is taken in parts of 64) and a tile of
+// two row sets of 64 weight rows (gate/up: the gate
 // rows and the up rows of 64 neurons; down: the two halves of 128 output
 // rows); wave w owns rows 16 (w % 4) .. +15 of row set w / 4. Every product
 // is a 16x16x32 MFMA (bf16 for gate/up, fp16 for down) with the expert's
@@ -51,6 +52,10 @@
 // Workgroups whose block lies past num_padded (read on the device) skip it,
 // so the grid can be sized from the host-known capacity. No floating-point
 // atomics; every sum has a fixed order.
+// H and I need only be multiples of 32: when a GEMM's K or output rows are
+// off the 128 grid, its last slab holds fewer MFMA steps and its last tile
+// reaches past the output rows (the kRagged instantiation handles both; the
+// loads stay inside their rows and the rows past the end are not written).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -208,8 +213,8 @@ constexpr int kMaxDepth = 8;
 
 // LDS ring of one GEMM instantiation. A slot holds one slab: the tile's 128
 // weight rows, 1 KB per (active sub-tile, step) of activations and, for the
-// down GEMM, a 1 KB page of chunk multipliers. Blocks of up to four
-// sub-tiles (b <= 64) get at least 64 KB and two slots at the largest slot
+// down GEMM, a 1 KB page of chunk multipliers. Tasks of up to four
+// sub-tiles (b > 16) get at least 64 KB and two slots at the largest slot
 // (two workgroups per CU); blocks of one sub-tile (b <= 16) get three int4
 // slots or two MXFP8 slots (three workgroups per CU).
 template <int kFmt, bool kGateUp, bool kSmall>
@@ -280,8 +285,8 @@ void grouped_gemm(const GemmParams p) {
     const int part = bp - blk * p.nparts;                 // 64-column part of the block
     const int cb = part * kMaxTok;                        // its first column within the block
     const int bw = min(p.b - cb, kMaxTok);                // and its columns
-    // Every wave holds the block's columns itself, lane c column c (b <= 64):
-    // rc is its route (batched layout: its row), -1 for padding, and bc the
+    // Every wave holds the task's columns itself, lane c column cb + c of the
+    // block: rc is its route (batched layout: its row), -1 for padding, and bc the
     // B row it reads. The expert ID and the routes are loaded together, and
     // the active sub-tiles, B rows and output rows come from ballots and
     // lane reads, with no LDS round trip or barrier before the first DMA.
