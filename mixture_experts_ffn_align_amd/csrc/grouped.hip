@@ -196,8 +196,9 @@ struct GemmParams {
   float* yhat;                   // down output [Mk][H]
   float* w13_out;                // gate/up: fp32 [Mk][2I] W13 outputs (gate, up) or null
   int mk, k, E, b, nblk;
-  int ntile;                     // weight tiles per part of a block
-  int nparts;                    // 64-column parts per block, ceil(b / 64)
+  int ntile;                     // weight tiles per block
+  int col0;                      // first column of every block this launch takes (blocks of more
+                                 // than 64 routes take one launch per 64 columns)
   int rows_per_expert;           // weight rows per expert (2I or H)
   int set_stride;                // row offset of row set 1 (I: up rows; 64: next 64 rows)
   int tile_stride;               // row offset between tiles (64 or 128)
@@ -265,8 +266,9 @@ void grouped_gemm(const GemmParams p) {
   const int rs = wave >> 2;                         // this wave's row set
   const int rl = 16 * (wave & 3);                   // first row of this wave within the set
   const int n = lane & 15, lq = lane >> 4;
-  const int per_blk = p.nparts * p.ntile;              // tasks per block
-  const int ntasks = p.nblk * per_blk;
+  const int ntasks = p.nblk * p.ntile;
+  const int cb = p.col0;                               // this launch's first column of each block
+  const int bw = min(p.b - cb, kMaxTok);               // and its columns
   const bool batched = p.counts != nullptr;
   const int npad = batched ? 0 : p.num_padded[0];
   const int row_bytes = kMx ? p.K : p.K / 2, gpr = p.K / p.g;
@@ -279,14 +281,11 @@ void grouped_gemm(const GemmParams p) {
   const uint32_t nib_mask = in_vgpr(kNibMask<kHalf>);
 
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
-    const int bp = task / p.ntile;                        // (block, part) index
-    const int ng = task - bp * p.ntile;
-    const int blk = p.nparts == 1 ? bp : bp / p.nparts;
-    const int part = bp - blk * p.nparts;                 // 64-column part of the block
-    const int cb = part * kMaxTok;                        // its first column within the block
-    const int bw = min(p.b - cb, kMaxTok);                // and its columns
+    const int blk = task / p.ntile;
+    const int ng = task - blk * p.ntile;
     // Every wave holds the task's columns itself, lane c column cb + c of the
-    // block: rc is its route (batched layout: its row), -1 for padding, and bc the
+    // block (cb: this launch's part): rc is its route (batched layout: its
+    // row), -1 for padding, and bc the
     // B row it reads. The expert ID and the routes are loaded together, and
     // the active sub-tiles, B rows and output rows come from ballots and
     // lane reads, with no LDS round trip or barrier before the first DMA.
@@ -806,13 +805,25 @@ hipError_t launch_gemm_ring(const GemmParams& gp_in, int wgs, hipStream_t stream
 // slots are small: the small ring keeps two or more slots in flight and lets
 // three workgroups share a CU (more tasks per round).
 template <bool kGateUp>
-hipError_t launch_gemm(int fmt, const GemmParams& gp, int wgs, hipStream_t stream) {
+hipError_t launch_gemm_part(int fmt, const GemmParams& gp, int wgs, hipStream_t stream) {
   if (fmt == MOE_W_MXFP8) {
     if (gp.b <= 16) return launch_gemm_ring<MOE_W_MXFP8, kGateUp, true>(gp, wgs, stream);
     return launch_gemm_ring<MOE_W_MXFP8, kGateUp, false>(gp, wgs, stream);
   }
   if (gp.b <= 16) return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, true>(gp, wgs, stream);
   return launch_gemm_ring<MOE_W_INT4_AWQ, kGateUp, false>(gp, wgs, stream);
+}
+
+// Blocks of more than 64 routes: one launch per 64 columns of every block
+// (the parts write disjoint rows of the output).
+template <bool kGateUp>
+hipError_t launch_gemm(int fmt, const GemmParams& gp_in, int wgs, hipStream_t stream) {
+  GemmParams gp = gp_in;
+  for (gp.col0 = 0; gp.col0 < gp.b; gp.col0 += kMaxTok) {
+    const hipError_t err = launch_gemm_part<kGateUp>(fmt, gp, wgs, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -849,14 +860,13 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& p, hipStream_t stream) {
   gp.b = p.b;
   gp.nblk = p.nblk;
   gp.ntile = (p.I + kTileRows - 1) / kTileRows;
-  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = 2 * p.I;
   gp.set_stride = p.I;
   gp.tile_stride = kTileRows;
   gp.out_rows = p.I;
   gp.K = p.H;
   gp.g = p.w13.group;
-  const int wgs = grid_for(int64_t(p.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<true>(p.w13.fmt, gp, wgs, stream);
 }
 
@@ -877,14 +887,13 @@ hipError_t launch_grouped_down(const GroupedArgs& p, hipStream_t stream) {
   gp.b = p.b;
   gp.nblk = p.nblk;
   gp.ntile = (p.H + 2 * kTileRows - 1) / (2 * kTileRows);
-  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = p.H;
   gp.set_stride = kTileRows;
   gp.tile_stride = 2 * kTileRows;
   gp.out_rows = p.H;
   gp.K = p.I;
   gp.g = p.w2.group;
-  const int wgs = grid_for(int64_t(p.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(p.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<false>(p.w2.fmt, gp, wgs, stream);
 }
 
@@ -905,14 +914,13 @@ hipError_t launch_grouped_gate_up_batched(const GroupedArgs& p, const int32_t* c
   gp.b = p.b;
   gp.nblk = p.E * gp.nbpe;
   gp.ntile = (p.I + kTileRows - 1) / kTileRows;
-  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = 2 * p.I;
   gp.set_stride = p.I;
   gp.tile_stride = kTileRows;
   gp.out_rows = p.I;
   gp.K = p.H;
   gp.g = p.w13.group;
-  const int wgs = grid_for(int64_t(gp.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<true>(p.w13.fmt, gp, wgs, stream);
 }
 
@@ -933,14 +941,13 @@ hipError_t launch_grouped_down_batched(const GroupedArgs& p, const int32_t* coun
   gp.b = p.b;
   gp.nblk = p.E * gp.nbpe;
   gp.ntile = (p.H + 2 * kTileRows - 1) / (2 * kTileRows);
-  gp.nparts = (p.b + kMaxTok - 1) / kMaxTok;
   gp.rows_per_expert = p.H;
   gp.set_stride = kTileRows;
   gp.tile_stride = 2 * kTileRows;
   gp.out_rows = p.H;
   gp.K = p.I;
   gp.g = p.w2.group;
-  const int wgs = grid_for(int64_t(gp.nblk) * gp.nparts * gp.ntile, p.max_workgroups);
+  const int wgs = grid_for(int64_t(gp.nblk) * gp.ntile, p.max_workgroups);
   return launch_gemm<false>(p.w2.fmt, gp, wgs, stream);
 }
 
