@@ -490,28 +490,32 @@ def copy_peak(nbytes=1 << 30, replays=5):
             "checked": ok, "us_per_loads_per_lane": per}
 
 
-MFMA_ITERS = 2048      # per wave and chain: about 0.9 ms per launch at the data-sheet rate
-MFMA_GRID = 2048       # workgroups of four waves: eight per CU
+MFMA_ITERS = 2048      # per wave and chain at 8 waves per CU: about 0.9 ms per launch
+MFMA_GRIDS = (256, 512, 1024, 2048)   # workgroups of four waves: one to eight per CU
 
 
-def mfma_peak(iters=MFMA_ITERS, grid=MFMA_GRID, replays=5):
+def mfma_peak(iters=MFMA_ITERS, grids=MFMA_GRIDS, replays=5):
     """Dense MFMA rate of the measurement library's MFMA kernel (16x16x32,
     bf16 and fp16 operands, fp32 accumulation, register operands, eight
-    independent chains per wave), each launch timed by its own start/end
-    events, median of replays. Each dtype is first run with every operand 1.0
-    and its per-wave sums checked exactly."""
+    independent chains per wave): the best over grids of one to eight
+    workgroups per CU (the same FLOPs per launch), each launch timed by its
+    own start/end events, median of replays. Each dtype is first run with
+    every operand 1.0 and its per-wave sums checked exactly, and 16 untimed
+    launches (about 15 ms of MFMA work) come before the timed ones."""
     import ctypes
     import torch
     import mixture_experts_ffn_align_amd as moe
     L = moe._binding.bench_lib()
+    grid = max(grids)
     sink = torch.zeros(4 * grid, dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
     a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)                          # creates the HIP events
     z.record(stream)
     torch.cuda.synchronize()
-    out = {"launch": f"{grid} workgroups x 4 waves x {iters} iterations x 8 independent chains of "
-                     f"16x16x32 MFMAs on register operands (seeded values in [1, 2))"}
+    out = {"launch": f"G workgroups x 4 waves x (iterations scaled so every G gives the FLOPs of {grid} x "
+                     f"{iters}) x 8 independent chains of 16x16x32 MFMAs on register operands (seeded values "
+                     f"in [1, 2)); G in {list(grids)}, best G reported"}
     for fp16, name in ((0, "bf16"), (1, "f16")):
         check_iters = 64
         sink.zero_()
@@ -519,18 +523,29 @@ def mfma_peak(iters=MFMA_ITERS, grid=MFMA_GRID, replays=5):
             raise RuntimeError("moe_bench_mfma failed")
         torch.cuda.synchronize()
         ok = bool(torch.all(sink == 8 * 32 * check_iters).item())
-        flops = ctypes.c_double(0.0)
-        times = []
-        for _ in range(replays + 1):          # the first call is untimed
-            if L.moe_bench_mfma(fp16, 1, iters, grid, sink.data_ptr(), ctypes.byref(flops), a.cuda_event,
-                                z.cuda_event, stream.cuda_stream) != 0:
+        # Untimed launches first, so that the clocks have settled under MFMA load.
+        for _ in range(16):
+            if L.moe_bench_mfma(fp16, 1, iters, grid, sink.data_ptr(), None, None, None, stream.cuda_stream) != 0:
                 raise RuntimeError("moe_bench_mfma failed")
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(z) * 1e3)
-        us = statistics.median(times[1:])
-        tf = flops.value / (us * 1e-6) / 1e12
+        torch.cuda.synchronize()
+        per_grid = {}
+        for gsz in grids:
+            it = iters * grid // gsz
+            flops = ctypes.c_double(0.0)
+            times = []
+            for _ in range(replays + 1):      # the first call is untimed
+                if L.moe_bench_mfma(fp16, 1, it, gsz, sink.data_ptr(), ctypes.byref(flops), a.cuda_event,
+                                    z.cuda_event, stream.cuda_stream) != 0:
+                    raise RuntimeError("moe_bench_mfma failed")
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(z) * 1e3)
+            us = statistics.median(times[1:])
+            per_grid[gsz] = (flops.value / (us * 1e-6) / 1e12, us)
+        best = max(per_grid, key=lambda gsz: per_grid[gsz][0])
+        tf, us = per_grid[best]
         out[name] = {"TFLOPs": round(tf, 1), "us": round(us, 2), "frac_of_datasheet": round(tf / BF16_PEAK_TFLOPS, 4),
-                     "checked": ok}
+                     "checked": ok, "best_grid": best,
+                     "TFLOPs_per_grid": {str(gsz): round(v[0], 1) for gsz, v in per_grid.items()}}
     del sink
     return out
 
