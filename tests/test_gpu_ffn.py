@@ -116,6 +116,9 @@ RAGGED = [
     dict(M=200, H=256, I=128, E=4, k=2, b=128, g=64),
     dict(M=150, H=320, I=160, E=3, k=2, b=96, g=32),
     dict(M=120, H=512, I=256, E=2, k=2, b=200, g=32, fmt="mxfp8"),
+    # The largest block the grouped path takes (1024 routes: sixteen parts),
+    # each of the two experts over a full block and a partly filled one.
+    dict(M=1100, H=256, I=128, E=2, k=2, b=1024, g=64),
     # The grouped small-block variant (int4, b <= 16, groups of 128 or
     # more, K <= 2048): nine gate/up slabs (the weight-load window refills
     # once), fifteen down slabs, and blocks filled to all 16 columns.
