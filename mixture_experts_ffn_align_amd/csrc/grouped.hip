@@ -316,6 +316,9 @@ void grouped_gemm(const GemmParams p) {
       if (((valid >> (16 * st)) & 0xFFFFull) != 0ull) amask |= 1 << st;
     }
     const int nact = __builtin_popcount(amask);
+    // A part of a block with no valid route has nothing to write (the same
+    // decision in every wave: all of them hold the same columns).
+    if (nact == 0) continue;
     int act[kSub];                    // sub-tile of each active index
     {
       int m = amask;
@@ -566,6 +569,17 @@ void grouped_gemm(const GemmParams p) {
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
           if (u >= nact) break;
+          // Every B operand of this sub-tile's steps is read before its first
+          // product (held in place by the scheduling barrier), so the chain
+          // waits on one LDS round trip instead of one per pair of steps.
+          uint4 Bs[kFlush];
+#pragma unroll
+          for (int jj = 0; jj < kFlush; ++jj) {
+            const int j = kFlush * f + jj;
+            Bs[jj] = *reinterpret_cast<const uint4*>(slot + kABytes + (u * kSteps + 2 * (j >> 1)) * 1024 +
+                                                     ((j & 1) ? boff_b1 : boff_b0));
+          }
+          __builtin_amdgcn_sched_barrier(0);
           float pm[2] = {1.0f, 1.0f};
           if constexpr (kHalf) {
             const float2 v = *reinterpret_cast<const float2*>(slot + page_off + 16 * (16 * u + n));
@@ -579,12 +593,9 @@ void grouped_gemm(const GemmParams p) {
             floatx4 d = {0, 0, 0, 0};
 #pragma unroll
             for (int jj = h * kPart; jj < (h + 1) * kPart; ++jj) {
-              const int j = kFlush * f + jj;
-              const uint4 B = *reinterpret_cast<const uint4*>(slot + kABytes + (u * kSteps + 2 * (j >> 1)) * 1024 +
-                                                              ((j & 1) ? boff_b1 : boff_b0));
               const uint4 Aj = kSub > 1 ? A[kSub > 1 ? jj : 0] : a_operand(jj);
-              d = mfma16<kHalf>(Aj, B, d);
-              if constexpr (!kMx) d = mfma16<kHalf>(Z, B, d);
+              d = mfma16<kHalf>(Aj, Bs[jj], d);
+              if constexpr (!kMx) d = mfma16<kHalf>(Z, Bs[jj], d);
             }
             if constexpr (kHalf) {
               const float m = pm[(kFlush * f + h * kPart) / 2];
