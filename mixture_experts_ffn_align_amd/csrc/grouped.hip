@@ -533,7 +533,9 @@ void grouped_gemm(const GemmParams p) {
       const int steps_here = kRagged && s == nslab - 1 ? last_steps : kSteps;
 #pragma unroll
       for (int f = 0; f < kSteps / kFlush; ++f) {
-        if (kFlush * f >= steps_here) break;
+        // (A guard rather than a break: the trip count stays exact, so the
+        // loop unrolls in every instantiation.)
+        if (kFlush * f < steps_here) {
         const int grp = grp0 + f;
         uint4 Z;
         float cs[4];
@@ -612,6 +614,7 @@ void grouped_gemm(const GemmParams p) {
           // reads, without the wait states that read needs (seen on gfx950
           // with ROCm 7.2: wrong sums for the last of two or three sub-tiles).
           asm volatile("" : "+v"(acc[u]));
+        }
         }
       }
       if (++gcount == spg) {
