@@ -89,14 +89,23 @@ __device__ __forceinline__ void scan_padded(const int* cnt, int* off, int* wtot,
   __syncthreads();
 }
 
-// Local experts of routes base + 1024 c + tid, c < kRegChunks (-1 past r1).
-// All the loads are issued before any is used.
+// Local experts of routes base + 1024 c + tid, c < kRegChunks (-1 past r1;
+// r1 > base). Every load is issued, unconditionally (routes past r1 read
+// route r1 - 1), before any is used: one memory round trip for the batch,
+// not one per chunk behind a branch.
 __device__ __forceinline__ void load_chunks(const int32_t* __restrict__ ids, int base, int r1, int E, int ebase,
                                             int (&ev)[kRegChunks]) {
+  int raw[kRegChunks];
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c) {
     const int r = base + c * kThreads + threadIdx.x;
-    ev[c] = r < r1 ? local_expert(ids, r, E, ebase) : -1;
+    raw[c] = ids[r < r1 ? r : r1 - 1];
+  }
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int r = base + c * kThreads + threadIdx.x;
+    const int e = raw[c] - ebase;
+    ev[c] = (r < r1 && e >= 0 && e < E) ? e : -1;
   }
 }
 
@@ -171,6 +180,9 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   const int tid = threadIdx.x;
   const int nblk = cap / b;
 
+  // The first batch of route IDs is requested before the prefill stores.
+  int ev[kRegChunks];
+  load_chunks(ids, 0, mk, E, ebase, ev);
   // Prefill: every row is padding and every block is past the end until the
   // steps below overwrite them (the ids loads are in flight meanwhile).
   for (int p = tid; p < cap; p += kThreads) sorted[p] = mk;
@@ -181,9 +193,8 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 
   // Histogram, kRegChunks chunks per batch of loads; up to kRegChunks
   // chunks of routes stay in registers for the placement.
-  int ev[kRegChunks];
   for (int base = 0; base < mk; base += kRegChunks * kThreads) {
-    load_chunks(ids, base, mk, E, ebase, ev);
+    if (base > 0) load_chunks(ids, base, mk, E, ebase, ev);
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c)
       if (ev[c] >= 0) atomicAdd(&cnt[ev[c]], 1);
